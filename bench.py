@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark: DF11 block decode on one MI355X.
+
+One step = one df11_decode_block launch over a whole transformer block (the
+Llama-3.1-8B-shaped block by default: q,k,v,o,gate,up,down, 218,103,808
+weights, one shared codebook), inputs resident in HBM.  Prints one JSON line.
+
+  value      decoded BF16 GB/s = 2 * weights * steps / timed seconds
+  roofline   algorithmic HBM bytes per launch (compressed sections read +
+             BF16 written) / average kernel time from HIP events, vs 8 TB/s
+  cpu_baseline  the oracle's unit-parallel bit-serial decode of the same block
+             on this host's cores (rank 0, N=1 only)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "huffman_decode_block_amd", "csrc", "df11_decode.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "df11_decode_kernel_c3_hbm_counters.json")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(s) -> dict:
+    """Bytes one decode must move: the compressed payload read once plus the
+    BF16 output written once (padding excluded)."""
+    rd = ((s.total_bits + 7) // 8          # encoded exponents
+          + s.n_total                      # sign/mantissa bytes
+          + (5 * s.n_windows + 7) // 8     # 5-bit gaps
+          + 8 * (s.n_units + 1)            # unit positions
+          + s.raw.tables_bytes)            # decode tables
+    wr = 2 * s.n_total
+    return {"read": int(rd), "write": int(wr), "total": int(rd + wr)}
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(sections, x, min_seconds: float) -> dict:
+    import numpy as np
+
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    enc = oracle.Encoded(n=int(sections.n_total), total_bits=int(sections.total_bits),
+                         n_windows=int(sections.n_windows), n_units=int(sections.n_units),
+                         code_len=sections.code_len, stream=sections.stream,
+                         sign_mant=sections.sign_mant, gaps=sections.gaps,
+                         unit_pos=sections.unit_pos, max_len=int(sections.max_code_len))
+    out = np.empty(enc.n, dtype=np.uint16)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_units(enc, threads=threads, out=out)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    ok = bool(np.array_equal(out, x))
+    return {"value": round(2.0 * enc.n * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole block ({enc.n} weights) decoded {reps}x by the oracle's bit-serial "
+                      f"tree walk, units split over {threads} threads; {el:.1f} s; output == input: {ok}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0 = library default)")
+    ap.add_argument("--max-groups", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the decode needs no cross-GPU exchange and "
+              "this build measures a single MI355X (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import df11_inputs as di
+    import huffman_decode_block_amd as hdb
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
+
+    wl = di.WORKLOADS[args.workload]
+    x = di.generate(args.workload)
+    enc = hdb.df11_encode_block(di.split(args.workload, x))
+    s = enc.sections
+    blk = hdb.DeviceBlock.from_encoded(enc, device=dev)
+    out = torch.empty(s.n_total, dtype=torch.bfloat16, device=dev)
+    launch = (args.waves, args.max_groups) if (args.waves or args.max_groups) else None
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        hdb.df11_decode_block(blk, out=out, stream=stream, launch=launch)
+    torch.cuda.synchronize()
+    # correctness of what is timed
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    if not torch.equal(out.view(torch.int16), xd):
+        raise SystemExit("decode is not bit-exact; refusing to report a number")
+    del xd
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        hdb.df11_decode_block(blk, out=out, stream=stream, launch=launch)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kt = sorted(a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends))
+    k_avg = sum(kt) / len(kt)
+
+    n = int(s.n_total)
+    ab = algorithmic_bytes(s)
+    achieved = ab["total"] / k_avg / 1e9
+    value = 2.0 * n * args.steps / wall / 1e9
+    traffic = measured_traffic()
+    res = {
+        "metric": "decoded BF16 GB/s and % HBM roofline per transformer block, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {wl.description}",
+            "weights": n,
+            "matrices": len(wl.mats),
+            "codebook": "shared per block" if wl.shared_codebook else "per matrix",
+            "seed": wl.seed,
+            "compressed_bytes": int(s.compressed_bytes),
+            "bits_per_weight": round(8 * ab["read"] / n, 3),
+            "mean_code_len_bits": round(s.mean_code_len_bits, 4),
+            "exp_entropy_bits": round(s.exp_entropy_bits, 4),
+            "max_code_len": int(s.max_code_len),
+            "decode_tables": int(s.n_tables),
+            "launch": {"waves_per_group": args.waves or "default", "max_groups": args.max_groups or "auto"},
+        },
+        "gweights_per_s": round(n * args.steps / wall / 1e9, 2),
+        "pct_hbm_roofline": round(100.0 * ab["total"] * args.steps / wall / 1e9 / PEAK_HBM_GBS, 2),
+        "kernel_us": {"avg": round(k_avg * 1e6, 2), "p10": round(kt[len(kt) // 10] * 1e6, 2),
+                      "p50": round(kt[len(kt) // 2] * 1e6, 2), "p90": round(kt[(9 * len(kt)) // 10] * 1e6, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ab["total"],
+            "kernel": "df11_decode_kernel",
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(s, x, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -210,3 +210,17 @@ def skewed(n: int, n_symbols: int, alpha: float, seed: int) -> np.ndarray:
 def random_normal(n: int, sigma: float, seed: int) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     return f32_to_bf16_bits(rng.standard_normal(n, dtype=np.float32) * np.float32(sigma))
+
+
+def many_subtables(r: int = 1000, seed: int = 127) -> np.ndarray:
+    """Exponent counts A: 300r, B: 2r and r for each of the other 254 values.
+
+    The Huffman code then has one 1-bit code, one 8-bit code and 254 9-bit
+    codes, which need 127 second-level decode tables."""
+    a, b = 127, 126
+    others = np.array([e for e in range(256) if e not in (a, b)], dtype=np.uint16)
+    exps = np.concatenate([np.full(300 * r, a, np.uint16), np.full(2 * r, b, np.uint16),
+                           np.repeat(others, r)])
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rng.shuffle(exps)
+    return from_exponents(exps, seed + 1)

@@ -1,0 +1,389 @@
+"""Python binding of libdf11 (include/df11.h): DFloat11 block encoding on the
+host and block decoding on an MI355X.
+
+Argument marshalling only: every step of the encoder runs in the library's
+C++ code and every step of the decode runs in its HIP kernel.  PyTorch is used
+for device memory and streams.  The functions keep the C names; a few small
+classes (Encoded, DeviceBlock) own the memory behind them.
+
+The library must be built first (``python -m huffman_decode_block_amd.build``
+or ``__graft_entry__.build()``); importing this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdf11.so")
+
+DF11_OK = 0
+DF11_E_INVALID_ARG = -1
+DF11_E_NOMEM = -2
+DF11_E_FORMAT = -3
+DF11_E_BUFFER_TOO_SMALL = -4
+DF11_E_UNSUPPORTED = -5
+DF11_E_HIP = -6
+DF11_FORMAT_VERSION = 1
+
+_u64 = ctypes.c_uint64
+_u32 = ctypes.c_uint32
+_vp = ctypes.c_void_p
+
+
+class df11_bf16_view(ctypes.Structure):
+    _fields_ = [("data", _vp), ("numel", _u64)]
+
+
+class df11_sections(ctypes.Structure):
+    _fields_ = [
+        ("version", _u32), ("n_mats", _u32), ("n_symbols", _u32), ("max_code_len", _u32),
+        ("n_tables", _u32), ("reserved", _u32),
+        ("n_total", _u64), ("total_bits", _u64), ("n_windows", _u64), ("n_units", _u64),
+        ("max_unit_count", _u64),
+        ("code_len", _vp), ("mat_offset", _vp),
+        ("stream", _vp), ("stream_bytes", _u64),
+        ("sign_mant", _vp), ("sign_mant_bytes", _u64),
+        ("gaps", _vp), ("gaps_bytes", _u64),
+        ("unit_pos", _vp),
+        ("tables", _vp), ("tables_bytes", _u64),
+        ("blob", _vp), ("blob_bytes", _u64),
+        ("off_code_len", _u64), ("off_mat_offset", _u64), ("off_stream", _u64),
+        ("off_sign_mant", _u64), ("off_gaps", _u64), ("off_unit_pos", _u64), ("off_tables", _u64),
+        ("exp_entropy_bits", ctypes.c_double), ("mean_code_len_bits", ctypes.c_double),
+    ]
+
+
+class df11_device_block(ctypes.Structure):
+    _fields_ = [
+        ("tables", _vp), ("tables_bytes", _u64),
+        ("stream", _vp), ("stream_bytes", _u64),
+        ("sign_mant", _vp), ("sign_mant_bytes", _u64),
+        ("gaps", _vp), ("gaps_bytes", _u64),
+        ("unit_pos", _vp),
+        ("n_total", _u64), ("total_bits", _u64), ("n_windows", _u64), ("n_units", _u64),
+        ("max_unit_count", _u64),
+        ("version", _u32), ("n_tables", _u32),
+    ]
+
+
+class df11_launch(ctypes.Structure):
+    _fields_ = [("waves_per_group", _u32), ("max_groups", _u32)]
+
+
+class DF11Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {df11_status_str(status)} ({status})")
+
+
+_lib = None
+
+EXPORTS = [
+    "df11_encode_block", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
+    "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
+    "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error",
+]
+
+
+def lib():
+    """The loaded libdf11 (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with python -m huffman_decode_block_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.df11_encode_block.argtypes = [P(df11_bf16_view), _u32, _u32, P(_vp)]
+    L.df11_encode_block.restype = ctypes.c_int32
+    L.df11_encoded_sections.argtypes = [_vp, P(df11_sections)]
+    L.df11_encoded_sections.restype = ctypes.c_int32
+    L.df11_encoded_free.argtypes = [_vp]
+    L.df11_encoded_free.restype = None
+    L.df11_validate.argtypes = [P(df11_sections)]
+    L.df11_validate.restype = ctypes.c_int32
+    L.df11_tables_size.argtypes = [_vp, P(_u64), P(_u32)]
+    L.df11_tables_size.restype = ctypes.c_int32
+    L.df11_build_tables.argtypes = [_vp, _vp, _u64]
+    L.df11_build_tables.restype = ctypes.c_int32
+    L.df11_device_block_from_blob.argtypes = [P(df11_sections), _vp, P(df11_device_block)]
+    L.df11_device_block_from_blob.restype = ctypes.c_int32
+    L.df11_decode_block.argtypes = [P(df11_device_block), _vp, _u64, _vp]
+    L.df11_decode_block.restype = ctypes.c_int32
+    L.df11_decode_block_ex.argtypes = [P(df11_device_block), _vp, _u64, _vp, P(df11_launch)]
+    L.df11_decode_block_ex.restype = ctypes.c_int32
+    L.df11_status_str.argtypes = [ctypes.c_int32]
+    L.df11_status_str.restype = ctypes.c_char_p
+    L.df11_last_hip_error.argtypes = []
+    L.df11_last_hip_error.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def df11_status_str(status: int) -> str:
+    return lib().df11_status_str(int(status)).decode()
+
+
+def df11_last_hip_error() -> int:
+    return int(lib().df11_last_hip_error())
+
+
+def _check(status: int, what: str):
+    if status != DF11_OK:
+        raise DF11Error(status, what)
+
+
+def _as_u16(m) -> np.ndarray:
+    """Raw BF16 bits of a host array / CPU tensor as a contiguous uint16 array."""
+    try:
+        import torch
+        if isinstance(m, torch.Tensor):
+            if m.is_cuda:
+                raise ValueError("the encoder takes host tensors")
+            if m.dtype == torch.bfloat16:
+                m = m.contiguous().view(torch.int16)
+            return m.contiguous().numpy().view(np.uint16).reshape(-1)
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(m)
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected BF16 bits (uint16/int16 or torch.bfloat16), got {a.dtype}")
+    return a.reshape(-1)
+
+
+def _np_view(ptr: int, count: int, dtype) -> np.ndarray:
+    if count == 0:
+        return np.zeros(0, dtype=dtype)
+    ctype = np.ctypeslib.as_ctypes_type(dtype)
+    arr = (ctype * count).from_address(ptr)
+    return np.ctypeslib.as_array(arr)
+
+
+class Sections:
+    """Numpy views of one encoded blob (valid while its Encoded lives)."""
+
+    def __init__(self, owner, s: df11_sections):
+        self._owner = owner
+        self.raw = s
+        self.version = s.version
+        self.n_mats = s.n_mats
+        self.n_symbols = s.n_symbols
+        self.max_code_len = s.max_code_len
+        self.n_tables = s.n_tables
+        self.n_total = s.n_total
+        self.total_bits = s.total_bits
+        self.n_windows = s.n_windows
+        self.n_units = s.n_units
+        self.max_unit_count = s.max_unit_count
+        self.exp_entropy_bits = s.exp_entropy_bits
+        self.mean_code_len_bits = s.mean_code_len_bits
+        self.code_len = _np_view(s.code_len, 256, np.uint8)
+        self.mat_offset = _np_view(s.mat_offset, s.n_mats + 1, np.uint64)
+        self.stream = _np_view(s.stream, s.stream_bytes, np.uint8)
+        self.sign_mant = _np_view(s.sign_mant, s.sign_mant_bytes, np.uint8)
+        self.gaps = _np_view(s.gaps, s.gaps_bytes, np.uint8)
+        self.unit_pos = _np_view(s.unit_pos, s.n_units + 1, np.uint64)
+        self.tables = _np_view(s.tables, s.tables_bytes, np.uint8)
+        self.blob = _np_view(s.blob, s.blob_bytes, np.uint8)
+
+    @property
+    def compressed_bytes(self) -> int:
+        """Bytes a decode reads: stream, sign/mantissa, gaps, positions, tables."""
+        return int(self.raw.stream_bytes + self.raw.sign_mant_bytes + self.raw.gaps_bytes
+                   + 8 * (self.n_units + 1) + self.raw.tables_bytes)
+
+
+class Encoded:
+    """Owner of a df11_encoded blob (host memory allocated by the library)."""
+
+    def __init__(self, handle: int):
+        self._h = handle
+        s = df11_sections()
+        _check(lib().df11_encoded_sections(handle, ctypes.byref(s)), "df11_encoded_sections")
+        self.sections = Sections(self, s)
+
+    def free(self):
+        if self._h:
+            lib().df11_encoded_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.free()
+
+
+def df11_encode_block(mats, n_threads: int = 0) -> Encoded:
+    """Encode a list of BF16 matrices (host) as one block with one codebook."""
+    arrays = [_as_u16(m) for m in mats]
+    views = (df11_bf16_view * max(1, len(arrays)))()
+    for i, a in enumerate(arrays):
+        views[i].data = a.ctypes.data if a.size else None
+        views[i].numel = a.size
+    h = _vp()
+    _check(lib().df11_encode_block(views, len(arrays), n_threads, ctypes.byref(h)), "df11_encode_block")
+    return Encoded(h.value)
+
+
+def df11_encoded_sections(enc: Encoded) -> Sections:
+    return enc.sections
+
+
+def df11_encoded_free(enc: Encoded) -> None:
+    enc.free()
+
+
+def df11_validate(sections: Sections) -> int:
+    """Host-side structural check; returns the status code."""
+    return int(lib().df11_validate(ctypes.byref(sections.raw)))
+
+
+def df11_tables_size(code_len) -> tuple:
+    cl = np.ascontiguousarray(np.asarray(code_len, dtype=np.uint8).reshape(256))
+    nb, nt = _u64(), _u32()
+    _check(lib().df11_tables_size(cl.ctypes.data, ctypes.byref(nb), ctypes.byref(nt)), "df11_tables_size")
+    return int(nb.value), int(nt.value)
+
+
+def df11_build_tables(code_len) -> np.ndarray:
+    cl = np.ascontiguousarray(np.asarray(code_len, dtype=np.uint8).reshape(256))
+    nb, _ = df11_tables_size(cl)
+    out = np.zeros(nb, dtype=np.uint8)
+    _check(lib().df11_build_tables(cl.ctypes.data, out.ctypes.data, nb), "df11_build_tables")
+    return out
+
+
+def df11_device_block_from_blob(sections: Sections, device_ptr: int) -> df11_device_block:
+    b = df11_device_block()
+    _check(lib().df11_device_block_from_blob(ctypes.byref(sections.raw), device_ptr, ctypes.byref(b)),
+           "df11_device_block_from_blob")
+    return b
+
+
+class DeviceBlock:
+    """An encoded block resident in device memory (torch tensors) plus the
+    df11_device_block that describes it."""
+
+    def __init__(self, raw: df11_device_block, keep: list, n_total: int, mat_offset=None):
+        self.raw = raw
+        self._keep = keep
+        self.n_total = int(n_total)
+        self.mat_offset = None if mat_offset is None else np.asarray(mat_offset, dtype=np.int64)
+
+    @classmethod
+    def from_encoded(cls, enc: Encoded, device="cuda") -> "DeviceBlock":
+        import torch
+        s = enc.sections
+        blob = torch.empty(int(s.raw.blob_bytes), dtype=torch.uint8, device=device)
+        blob.copy_(torch.from_numpy(s.blob))
+        raw = df11_device_block_from_blob(s, blob.data_ptr())
+        return cls(raw, [blob], s.n_total, s.mat_offset.copy())
+
+    @classmethod
+    def from_parts(cls, *, code_len, stream, sign_mant, gaps, unit_pos, n_total, total_bits,
+                   device="cuda") -> "DeviceBlock":
+        """Device block from separately given host sections (for example the
+        oracle's); the decode tables are built here from code_len."""
+        import torch
+        tables = df11_build_tables(code_len)
+        _, n_tables = df11_tables_size(code_len)
+        up = np.ascontiguousarray(unit_pos, dtype=np.uint64)
+        parts = {}
+        for name, arr in [("tables", tables), ("stream", stream), ("sign_mant", sign_mant),
+                          ("gaps", gaps), ("unit_pos", up.view(np.uint8))]:
+            a = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+            t = torch.empty(max(1, a.size), dtype=torch.uint8, device=device)
+            if a.size:
+                t[:a.size].copy_(torch.from_numpy(a))
+            parts[name] = (t, a.size)
+        b = df11_device_block()
+        b.tables, b.tables_bytes = parts["tables"][0].data_ptr(), parts["tables"][1]
+        b.stream, b.stream_bytes = parts["stream"][0].data_ptr(), parts["stream"][1]
+        b.sign_mant, b.sign_mant_bytes = parts["sign_mant"][0].data_ptr(), parts["sign_mant"][1]
+        b.gaps, b.gaps_bytes = parts["gaps"][0].data_ptr(), parts["gaps"][1]
+        b.unit_pos = parts["unit_pos"][0].data_ptr()
+        b.n_total = int(n_total)
+        b.total_bits = int(total_bits)
+        b.n_windows = (int(total_bits) + 63) // 64
+        b.n_units = (b.n_windows + 63) // 64
+        d = np.diff(up.astype(np.int64))
+        b.max_unit_count = int(d.max()) if d.size else 0
+        b.version = DF11_FORMAT_VERSION
+        b.n_tables = n_tables
+        return cls(b, [t for t, _ in parts.values()], n_total)
+
+    def compressed_bytes(self) -> int:
+        r = self.raw
+        return int(r.stream_bytes + r.sign_mant_bytes + r.gaps_bytes + 8 * (r.n_units + 1) + r.tables_bytes)
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def df11_decode_block(block: DeviceBlock, out=None, stream=None, launch=None):
+    """Decode `block` into `out` (a flat torch.bfloat16 device tensor with at
+    least n_total elements; allocated when None) on `stream` (torch stream,
+    raw handle, or None for the current stream).  Returns out."""
+    import torch
+    if out is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+        out = torch.empty(max(1, block.n_total), dtype=torch.bfloat16, device=dev)
+    if out.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not out.is_cuda:
+        raise TypeError("out must be a 16-bit device tensor")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    h = _stream_handle(stream, out.device)
+    if launch is None:
+        st = lib().df11_decode_block(ctypes.byref(block.raw), out.data_ptr(), out.numel(), h)
+    else:
+        L = df11_launch(*launch) if not isinstance(launch, df11_launch) else launch
+        st = lib().df11_decode_block_ex(ctypes.byref(block.raw), out.data_ptr(), out.numel(), h,
+                                        ctypes.byref(L))
+    _check(st, "df11_decode_block")
+    return out
+
+
+def df11_decode_block_ex(block: DeviceBlock, out=None, stream=None, waves_per_group=0, max_groups=0):
+    return df11_decode_block(block, out, stream, launch=(waves_per_group, max_groups))
+
+
+def matrix_views(out, block_or_offsets, shapes=None):
+    """Per-matrix views of a decoded block output."""
+    off = block_or_offsets.mat_offset if hasattr(block_or_offsets, "mat_offset") else block_or_offsets
+    off = [int(v) for v in off]
+    views = []
+    for i in range(len(off) - 1):
+        v = out[off[i]:off[i + 1]]
+        if shapes is not None:
+            v = v.view(*shapes[i])
+        views.append(v)
+    return views
+
+
+__all__ = [
+    "df11_encode_block", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
+    "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
+    "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "Encoded", "Sections",
+    "DeviceBlock", "DF11Error", "matrix_views", "lib",
+]
+
+# Load eagerly: the package is unusable without its native library.
+lib()

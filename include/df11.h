@@ -1,0 +1,206 @@
+/*
+ * df11.h -- C-ABI of libdf11: DFloat11 (DF11) block encoding on the host and
+ * block decoding on an AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (from the pages on DFloat11):
+ *  - hada.io summary of the DFloat11 paper, section "Le format DFloat11": only
+ *    the 8-bit exponent of each BF16 weight is entropy coded, with a Huffman
+ *    code built from the exponent distribution; the codes are bit-packed into
+ *    an EncodedExponent byte array and the sign and 7-bit mantissa are kept
+ *    verbatim in a PackedSignMantissa byte array.
+ *  - same page, section "Noyau GPU en deux etapes et metadonnees
+ *    auxiliaires": each GPU thread owns 8 consecutive bytes (64 bits) of the
+ *    encoded exponents and decodes the codes that start in them; a 5-bit gap
+ *    per thread gives the offset of its first code; output positions are
+ *    stored only once per group of threads; the kernel counts in a first
+ *    phase, prefix-sums the counts, decodes again in a second phase into an
+ *    on-chip buffer and writes it out coalesced.
+ *  - same page, section "Decompression par bloc transformer": all matrices of
+ *    one transformer block are decoded together in one launch.
+ *  - chatpaper.ai abstract of the DFloat11 paper: the decoded weights are
+ *    bit-for-bit identical to the original BF16 weights.
+ *
+ * Format version 1 (readings of points the pages leave open):
+ *  - A block is the concatenation of its matrices (row-major, in the order
+ *    given), with one codebook for the whole block.
+ *  - Code lengths: Huffman with ties broken by (weight, creation order), where
+ *    leaves are ordered by (count, exponent) and precede merged nodes; if a
+ *    code would exceed 32 bits the lengths come from package-merge with cap 32
+ *    (a leaf precedes a package of equal weight).  A one-symbol alphabet gets
+ *    length 1.
+ *  - Canonical codewords: symbols in (length, exponent) order, first code 0,
+ *    next = (prev + 1) << (length step).
+ *  - Stream bit j is bit (7 - j % 8) of byte j / 8 (MSB first).
+ *  - sign_mant[i] = (sign << 7) | mantissa.
+ *  - Window w = stream bits [64w, 64w + 64).  gap[w] = first code start at or
+ *    after 64w, minus 64w; total_bits - 64w when none (only possible in the
+ *    last window).  Always in [0, 31].  Packed as 5-bit fields, MSB first,
+ *    field w at bits [5w, 5w + 5).
+ *  - Unit u = windows [64u, 64u + 64) (one 64-lane wavefront).
+ *    unit_pos[u] = number of codes starting before bit 4096u, for
+ *    u < n_units, and unit_pos[n_units] = n_total.
+ *  - Section sizes: stream 512 * n_units + 16 bytes, sign_mant
+ *    round_up(n_total, 16) bytes, gaps 40 * n_units + 8 bytes, unit_pos
+ *    n_units + 1 entries; all padding is zero.
+ *
+ * Threading: encoder calls are re-entrant.  Decode calls are stream ordered;
+ * concurrent decodes into distinct outputs are safe.
+ */
+#ifndef DF11_H
+#define DF11_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DF11_FORMAT_VERSION 1u
+#define DF11_WINDOW_BITS 64u        /* 8 bytes of encoded exponents per thread */
+#define DF11_UNIT_WINDOWS 64u       /* windows per stored output position */
+#define DF11_MAX_CODE_LEN 32u
+#define DF11_MAX_UNIT_WEIGHTS 4096u /* 64 windows x at most 64 code starts */
+
+typedef int32_t df11_status;
+#define DF11_OK 0
+#define DF11_E_INVALID_ARG (-1)      /* null pointer, bad size or alignment */
+#define DF11_E_NOMEM (-2)            /* host allocation failed */
+#define DF11_E_FORMAT (-3)           /* sections are inconsistent */
+#define DF11_E_BUFFER_TOO_SMALL (-4) /* caller buffer shorter than needed */
+#define DF11_E_UNSUPPORTED (-5)      /* version or feature not supported */
+#define DF11_E_HIP (-6)              /* the HIP runtime reported an error */
+
+/* A host view of raw BF16 bit patterns (caller-owned, read only). */
+typedef struct df11_bf16_view {
+    const uint16_t *data;
+    uint64_t numel;
+} df11_bf16_view;
+
+/* An encoded block: one library-owned host allocation (the "blob") holding
+ * every section at a 256-byte aligned offset.  Opaque. */
+typedef struct df11_encoded df11_encoded;
+
+/* Host views into an encoded blob, valid until df11_encoded_free.  Every
+ * off_* field is the byte offset of that section inside the blob, so a device
+ * copy of the whole blob can be addressed with the same offsets. */
+typedef struct df11_sections {
+    uint32_t version;
+    uint32_t n_mats;
+    uint32_t n_symbols;             /* exponents with a nonzero count */
+    uint32_t max_code_len;          /* longest codeword, bits */
+    uint32_t n_tables;              /* 256-entry decode tables (root first) */
+    uint32_t reserved;
+    uint64_t n_total;               /* weights in the block */
+    uint64_t total_bits;            /* sum of all codeword lengths */
+    uint64_t n_windows;             /* ceil(total_bits / 64) */
+    uint64_t n_units;               /* ceil(n_windows / 64) */
+    uint64_t max_unit_count;        /* max over u of unit_pos[u+1] - unit_pos[u] */
+    const uint8_t *code_len;        /* [256]; 0 = exponent absent */
+    const uint64_t *mat_offset;     /* [n_mats + 1] element offsets */
+    const uint8_t *stream;          /* EncodedExponent */
+    uint64_t stream_bytes;
+    const uint8_t *sign_mant;       /* PackedSignMantissa */
+    uint64_t sign_mant_bytes;
+    const uint8_t *gaps;            /* 5-bit gap fields */
+    uint64_t gaps_bytes;
+    const uint64_t *unit_pos;       /* [n_units + 1] */
+    const uint8_t *tables;          /* decode tables built from code_len */
+    uint64_t tables_bytes;
+    const uint8_t *blob;
+    uint64_t blob_bytes;
+    uint64_t off_code_len, off_mat_offset, off_stream, off_sign_mant, off_gaps, off_unit_pos,
+        off_tables;
+    double exp_entropy_bits;        /* Shannon entropy of the exponents, bits/weight */
+    double mean_code_len_bits;      /* total_bits / n_total */
+} df11_sections;
+
+/* Encodes the concatenation of n_mats BF16 matrices with one shared codebook.
+ * mats: host views, caller-owned, read only.  n_threads: host threads to use
+ * (0 = all CPUs the process may run on).  *out receives a new blob that the
+ * caller releases with df11_encoded_free.  n_mats may be 0 and views may be
+ * empty (an empty block is valid).  Errors: DF11_E_INVALID_ARG (null
+ * pointers), DF11_E_NOMEM. */
+df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_mats, uint32_t n_threads,
+                              df11_encoded **out);
+
+/* Fills *out with views into enc.  Errors: DF11_E_INVALID_ARG. */
+df11_status df11_encoded_sections(const df11_encoded *enc, df11_sections *out);
+
+/* Releases a blob from df11_encode_block (NULL is ignored). */
+void df11_encoded_free(df11_encoded *enc);
+
+/* Host-side structural check of the sections (sizes, code lengths form a
+ * prefix code of at most 32 bits, gaps within [0, 31] and consistent with
+ * total_bits, unit_pos non-decreasing from 0 to n_total, max_unit_count,
+ * decode tables equal to the ones built from code_len).  It does not decode
+ * the stream.  Returns DF11_OK or DF11_E_FORMAT / DF11_E_INVALID_ARG. */
+df11_status df11_validate(const df11_sections *s);
+
+/* Decode tables for the GPU kernel, derived from the 256 code lengths: a
+ * hierarchy of 256-entry tables indexed by 8 stream bits each (the pages'
+ * compact LUTs, section "Decodage fonde sur des LUT hierarchiques"), with
+ * 32-bit entries.  df11_tables_size reports the bytes needed and the table
+ * count; df11_build_tables writes them to dst (host memory, dst_bytes at
+ * least that size).  Errors: DF11_E_INVALID_ARG, DF11_E_FORMAT (lengths do
+ * not form a prefix code of at most 32 bits), DF11_E_BUFFER_TOO_SMALL. */
+df11_status df11_tables_size(const uint8_t code_len[256], uint64_t *bytes, uint32_t *n_tables);
+df11_status df11_build_tables(const uint8_t code_len[256], void *dst, uint64_t dst_bytes);
+
+/* Device-side description of one encoded block.  Every pointer is device
+ * memory owned by the caller (for example torch tensors), 16-byte aligned,
+ * and must stay valid until the decode has run on its stream. */
+typedef struct df11_device_block {
+    const void *tables;
+    uint64_t tables_bytes;
+    const uint8_t *stream;
+    uint64_t stream_bytes;
+    const uint8_t *sign_mant;
+    uint64_t sign_mant_bytes;
+    const uint8_t *gaps;
+    uint64_t gaps_bytes;
+    const uint64_t *unit_pos;
+    uint64_t n_total, total_bits, n_windows, n_units, max_unit_count;
+    uint32_t version;
+    uint32_t n_tables;
+} df11_device_block;
+
+/* Fills *out for a device copy of a whole blob starting at device_blob. */
+df11_status df11_device_block_from_blob(const df11_sections *s, const void *device_blob,
+                                        df11_device_block *out);
+
+/* Decodes the block into out_bf16[0 .. n_total) (device memory, 16-byte
+ * aligned, out_capacity elements).  One kernel launch on the HIP stream
+ * `hip_stream` (a hipStream_t; NULL = the null stream); the call does not
+ * synchronize and allocates nothing.  Exactly n_total elements are written;
+ * nothing else is touched.  Argument, capacity, alignment and version errors
+ * are reported synchronously (DF11_E_INVALID_ARG, DF11_E_BUFFER_TOO_SMALL,
+ * DF11_E_UNSUPPORTED); a launch failure returns DF11_E_HIP.  Corrupted
+ * section contents are not detected on the device, but every store stays in
+ * [0, n_total) and every loop is bounded.  n_total = 0 is a no-op. */
+df11_status df11_decode_block(const df11_device_block *blk, uint16_t *out_bf16,
+                              uint64_t out_capacity, void *hip_stream);
+
+/* Launch geometry for df11_decode_block_ex (0 = automatic). */
+typedef struct df11_launch {
+    uint32_t waves_per_group;  /* 64-lane waves per workgroup: 1, 2, 4, 8 or 16 */
+    uint32_t max_groups;       /* cap on the grid size (persistent workgroups) */
+} df11_launch;
+
+/* df11_decode_block with an explicit launch geometry; the output does not
+ * depend on it. */
+df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf16,
+                                 uint64_t out_capacity, void *hip_stream,
+                                 const df11_launch *launch);
+
+/* Text for a status code (static storage). */
+const char *df11_status_str(df11_status s);
+
+/* The last HIP error code recorded by a failing decode call in this thread
+ * (0 if none). */
+int32_t df11_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DF11_H */
