@@ -7,7 +7,8 @@ for device memory and streams.  The functions keep the C names; a few small
 classes (Encoded, DeviceBlock) own the memory behind them.
 
 The library must be built first (``python -m huffman_decode_block_amd.build``
-or ``__graft_entry__.build()``); importing this package without it raises.
+or ``__graft_entry__.build()``); the first call into the package raises
+ImportError when it is missing.  There is no fallback path.
 """
 from __future__ import annotations
 
@@ -84,7 +85,7 @@ _lib = None
 EXPORTS = [
     "df11_encode_block", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
-    "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error",
+    "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
 ]
 
 
@@ -119,6 +120,8 @@ def lib():
     L.df11_status_str.restype = ctypes.c_char_p
     L.df11_last_hip_error.argtypes = []
     L.df11_last_hip_error.restype = ctypes.c_int32
+    L.df11_hip_error_name.argtypes = [ctypes.c_int32]
+    L.df11_hip_error_name.restype = ctypes.c_char_p
     _lib = L
     return L
 
@@ -131,8 +134,15 @@ def df11_last_hip_error() -> int:
     return int(lib().df11_last_hip_error())
 
 
+def df11_hip_error_name(code: int) -> str:
+    return lib().df11_hip_error_name(int(code)).decode()
+
+
 def _check(status: int, what: str):
     if status != DF11_OK:
+        if status == DF11_E_HIP:
+            code = df11_last_hip_error()
+            what = f"{what} [HIP error {code}: {df11_hip_error_name(code)}]"
         raise DF11Error(status, what)
 
 
@@ -381,9 +391,7 @@ def matrix_views(out, block_or_offsets, shapes=None):
 __all__ = [
     "df11_encode_block", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
-    "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "Encoded", "Sections",
+    "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
+    "Encoded", "Sections",
     "DeviceBlock", "DF11Error", "matrix_views", "lib",
 ]
-
-# Load eagerly: the package is unusable without its native library.
-lib()

@@ -220,8 +220,11 @@ int cu_count(int dev) {
     if (dev < 0 || dev >= 64) return 256;
     if (!g_dev[dev].cus) {
         int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
             v = 256;
+        }
+        if (v <= 0) v = 256;
         g_dev[dev].cus = v;
     }
     return g_dev[dev].cus;
@@ -252,6 +255,10 @@ df11_status check_block(const df11_device_block *b, const uint16_t *out, uint64_
 }  // namespace
 
 extern "C" int32_t df11_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" const char *df11_hip_error_name(int32_t code) {
+    return hipGetErrorName(static_cast<hipError_t>(code));
+}
 
 extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf16,
                                             uint64_t out_capacity, void *hip_stream,
@@ -288,22 +295,21 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
                                  : reinterpret_cast<const void *>(&df11_decode_kernel<false>);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, static_cast<int>(64 * waves),
-                                                     lds_bytes) != hipSuccess ||
-        per_cu <= 0)
+                                                     lds_bytes) != hipSuccess) {
+        (void)hipGetLastError();  // our own failed query: do not leave it to the caller
         per_cu = 1;
+    }
+    if (per_cu <= 0) per_cu = 1;
     const uint64_t groups = (blk->n_units + waves - 1) / waves;
     uint64_t grid = std::min<uint64_t>(groups, uint64_t(cu_count(dev)) * uint64_t(per_cu));
     if (launch && launch->max_groups) grid = std::min<uint64_t>(grid, launch->max_groups);
     grid = std::max<uint64_t>(grid, 1);
 
-    hipStream_t st = static_cast<hipStream_t>(hip_stream);
-    if (deep_global)
-        hipLaunchKernelGGL(df11_decode_kernel<true>, dim3(static_cast<uint32_t>(grid)), dim3(64 * waves),
-                           lds_bytes, st, p);
-    else
-        hipLaunchKernelGGL(df11_decode_kernel<false>, dim3(static_cast<uint32_t>(grid)), dim3(64 * waves),
-                           lds_bytes, st, p);
-    const hipError_t err = hipGetLastError();
+    // hipLaunchKernel reports the status of this launch only (hipGetLastError
+    // would also return errors left behind by earlier runtime calls).
+    void *args[] = {&p};
+    const hipError_t err = hipLaunchKernel(fn, dim3(static_cast<uint32_t>(grid)), dim3(64 * waves), args,
+                                           lds_bytes, static_cast<hipStream_t>(hip_stream));
     if (err != hipSuccess) {
         g_last_hip_error = static_cast<int32_t>(err);
         return DF11_E_HIP;

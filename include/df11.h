@@ -196,8 +196,9 @@ df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf1
 const char *df11_status_str(df11_status s);
 
 /* The last HIP error code recorded by a failing decode call in this thread
- * (0 if none). */
+ * (0 if none), and the HIP runtime's name for a HIP error code. */
 int32_t df11_last_hip_error(void);
+const char *df11_hip_error_name(int32_t code);
 
 #ifdef __cplusplus
 }
