@@ -91,6 +91,10 @@ def main():
     ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3", "C4", "C5"])
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0 = library default)")
     ap.add_argument("--max-groups", type=int, default=0)
+    ap.add_argument("--oversubscribe", type=int, default=0,
+                    help="workgroups per resident workgroup slot (0 = library default)")
+    ap.add_argument("--variant", type=int, default=0,
+                    help="1 = one code per lookup, 2 = multi-code lookups (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -127,7 +131,8 @@ def main():
     s = enc.sections
     blk = hdb.DeviceBlock.from_encoded(enc, device=dev)
     out = torch.empty(s.n_total, dtype=torch.bfloat16, device=dev)
-    launch = (args.waves, args.max_groups) if (args.waves or args.max_groups) else None
+    launch = (args.waves, args.max_groups, args.variant, args.oversubscribe) \
+        if (args.waves or args.max_groups or args.variant or args.oversubscribe) else None
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(args.warmup):
@@ -182,7 +187,10 @@ def main():
             "exp_entropy_bits": round(s.exp_entropy_bits, 4),
             "max_code_len": int(s.max_code_len),
             "decode_tables": int(s.n_tables),
-            "launch": {"waves_per_group": args.waves or "default", "max_groups": args.max_groups or "auto"},
+            "launch": {"waves_per_group": args.waves or "default", "max_groups": args.max_groups or "auto",
+                       "oversubscribe": args.oversubscribe or "default",
+                       "variant": {0: "default (multi-code)", 1: "one code per lookup",
+                                   2: "multi-code"}[args.variant]},
         },
         "gweights_per_s": round(n * args.steps / wall / 1e9, 2),
         "pct_hbm_roofline": round(100.0 * ab["total"] * args.steps / wall / 1e9 / PEAK_HBM_GBS, 2),

@@ -71,7 +71,11 @@ class df11_device_block(ctypes.Structure):
 
 
 class df11_launch(ctypes.Structure):
-    _fields_ = [("waves_per_group", _u32), ("max_groups", _u32)]
+    _fields_ = [("waves_per_group", _u32), ("max_groups", _u32), ("variant", _u32), ("oversubscribe", _u32)]
+
+
+DF11_VARIANT_SINGLE = 1
+DF11_VARIANT_MULTI = 2
 
 
 class DF11Error(RuntimeError):
@@ -364,15 +368,16 @@ def df11_decode_block(block: DeviceBlock, out=None, stream=None, launch=None):
     if launch is None:
         st = lib().df11_decode_block(ctypes.byref(block.raw), out.data_ptr(), out.numel(), h)
     else:
-        L = df11_launch(*launch) if not isinstance(launch, df11_launch) else launch
+        L = launch if isinstance(launch, df11_launch) else df11_launch(*launch)
         st = lib().df11_decode_block_ex(ctypes.byref(block.raw), out.data_ptr(), out.numel(), h,
                                         ctypes.byref(L))
     _check(st, "df11_decode_block")
     return out
 
 
-def df11_decode_block_ex(block: DeviceBlock, out=None, stream=None, waves_per_group=0, max_groups=0):
-    return df11_decode_block(block, out, stream, launch=(waves_per_group, max_groups))
+def df11_decode_block_ex(block: DeviceBlock, out=None, stream=None, waves_per_group=0, max_groups=0,
+                         variant=0, oversubscribe=0):
+    return df11_decode_block(block, out, stream, launch=(waves_per_group, max_groups, variant, oversubscribe))
 
 
 def matrix_views(out, block_or_offsets, shapes=None):

@@ -52,8 +52,8 @@ extern "C" df11_status df11_validate(const df11_sections *s) {
     if (s->n_total && ns == 0) return DF11_E_FORMAT;
     uint32_t nt = 0;
     if (df11i::build_tables(s->code_len, nullptr, 0, &nt) != DF11_OK) return DF11_E_FORMAT;
-    if (s->n_tables != nt || s->tables_bytes != uint64_t{nt} * 1024) return DF11_E_FORMAT;
-    std::vector<uint32_t> t(uint64_t{nt} * 256);
+    if (s->n_tables != nt || s->tables_bytes != df11i::tables_bytes_for(nt)) return DF11_E_FORMAT;
+    std::vector<uint32_t> t(df11i::tables_bytes_for(nt) / 4);
     df11i::build_tables(s->code_len, t.data(), t.size(), nullptr);
     if (std::memcmp(t.data(), s->tables, s->tables_bytes) != 0) return DF11_E_FORMAT;
     // unit positions

@@ -32,7 +32,7 @@
 namespace {
 
 constexpr uint32_t kLdsTableMax = 32;     // sub-tables beyond this stay in global memory
-constexpr uint32_t kMaxLdsBytes = 65536;  // per workgroup
+constexpr uint32_t kDefaultOversubscribe = 4;
 
 struct KParams {
     const uint32_t *tables;
@@ -93,6 +93,23 @@ __device__ __forceinline__ void consume(uint32_t e, uint32_t &h, uint32_t &l, ui
     r = __builtin_amdgcn_alignbit(r, 0u, e);
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (cross-lane moves inside the VALU, no LDS round trip):
+// shifts by 1, 2, 3 then 4 and 8 give the scan within each row of 16 lanes;
+// broadcasting lane 15 into rows 1 and 3, then lane 31 into rows 2 and 3,
+// carries the row totals across.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    uint32_t s = x;
+    s += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+    s += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+    s += __builtin_amdgcn_update_dpp(0u, x, 0x113, 0xF, 0xF, true);  // row_shr:3
+    s += __builtin_amdgcn_update_dpp(0u, s, 0x114, 0xF, 0xE, false); // row_shr:4, lanes 4..15 of a row
+    s += __builtin_amdgcn_update_dpp(0u, s, 0x118, 0xF, 0xC, false); // row_shr:8, lanes 8..15 of a row
+    s += __builtin_amdgcn_update_dpp(0u, s, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
+    s += __builtin_amdgcn_update_dpp(0u, s, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
+    return s;
+}
+
 // Two BF16 values from two staged (exponent << 7) halves and the sign/mantissa
 // bytes selected by `sel`: the byte permute puts each sm byte in both bytes
 // of its 16-bit slot, so bit 15 = sign and bits 6..0 = mantissa.
@@ -101,106 +118,280 @@ __device__ __forceinline__ uint32_t merge2(uint32_t staged, uint32_t sm4, uint32
     return (dup & 0x807F807Fu) | (staged & 0x7F807F80u);
 }
 
+// One code through the hierarchical tables, consumed; returns its entry.
 template <bool kDeepGlobal>
-__global__ void __launch_bounds__(1024) df11_decode_kernel(KParams p) {
+__device__ __forceinline__ uint32_t single_step(const uint32_t *lut, const KParams &p, uint32_t &h,
+                                                uint32_t &l, uint32_t &r) {
+    const uint32_t e = lookup<kDeepGlobal>(lut, p.tables, p.n_tables, h);
+    consume(e, h, l, r);
+    return e;
+}
+
+__device__ __forceinline__ int entry_length(uint32_t e) { return static_cast<int>((e >> 8) & 31u) + 1; }
+
+// Phase 1, one code per lookup: count the codes that start in [pos, end).
+template <bool kDeepGlobal>
+__device__ __forceinline__ uint32_t count_single(const uint32_t *lut, const KParams &p, uint32_t h,
+                                                 uint32_t l, uint32_t r, int pos, int end) {
+    uint32_t cnt = 0;
+    while (pos < end) {
+        pos += entry_length(single_step<kDeepGlobal>(lut, p, h, l, r));
+        ++cnt;
+    }
+    return cnt;
+}
+
+// Phase 1 with the count table: every lookup takes all the codes that end
+// inside the next 11 bits; only those starting before the window end (rem
+// bits from here) are counted.  `S` holds the window from the current code
+// start, followed by zeros instead of the 4-byte halo: only the last code
+// that starts inside the window can reach past it, and as the code is prefix
+// free, its zero-padded decode is longer than the window bits it covers, so
+// the next start it implies lies past the end and is not counted.
+template <bool kDeepGlobal>
+__device__ __forceinline__ uint32_t count_multi(const uint32_t *lut, const uint32_t *ct, const KParams &p,
+                                                uint64_t S, int rem) {
+    uint32_t cnt = 0;
+    while (rem > 0) {
+        const uint32_t top = static_cast<uint32_t>(S >> 32);
+        const uint32_t e = ct[top >> (32 - df11i::kCountBits)];
+        if (__builtin_expect(e == 0u, 0)) {  // first code longer than the index
+            const int len = entry_length(lookup<kDeepGlobal>(lut, p.tables, p.n_tables, top));
+            S <<= len;
+            rem -= len;
+            ++cnt;
+            continue;
+        }
+        const uint32_t w = rem < static_cast<int>(df11i::kCountBits) ? static_cast<uint32_t>(rem)
+                                                                    : df11i::kCountBits;
+        cnt += __popc(__builtin_amdgcn_ubfe(e, 20u, w));
+        S <<= (e & 63u);
+        rem -= static_cast<int>(e & 63u);
+    }
+    return cnt;
+}
+
+// Phase 2, one code per lookup: stage n values starting at dst.
+template <bool kDeepGlobal>
+__device__ __forceinline__ void emit_single(const uint32_t *lut, const KParams &p, uint32_t h, uint32_t l,
+                                            uint32_t r, uint16_t *dst, uint32_t n) {
+    for (uint32_t j = 0; j < n; ++j) dst[j] = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
+}
+
+// Phase 2 with the emit table: up to three codes per lookup.  While at least
+// three values remain, all three slots are written (slots past the codes
+// actually taken belong to this lane and are overwritten next); the last
+// one or two values go through the single-code path.
+template <bool kDeepGlobal>
+__device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et, const KParams &p, uint32_t h,
+                                           uint32_t l, uint32_t r, uint16_t *dst, uint32_t n) {
+    while (n >= 3) {
+        const uint64_t ev = *reinterpret_cast<const uint64_t *>(et + (h >> (32 - df11i::kEmitBits)));
+        const uint2 e = make_uint2(static_cast<uint32_t>(ev), static_cast<uint32_t>(ev >> 32));
+        const uint32_t k = (e.y >> 10) & 3u;
+        if (__builtin_expect(k == 0u, 0)) {  // first code longer than the index
+            *dst++ = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
+            --n;
+            continue;
+        }
+        dst[0] = static_cast<uint16_t>(e.x);
+        dst[1] = static_cast<uint16_t>(e.x >> 16);
+        dst[2] = static_cast<uint16_t>(e.y >> 16);
+        consume(e.y, h, l, r);
+        dst += k;
+        n -= k;
+    }
+    for (; n > 0; --n) *dst++ = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
+}
+
+// The count and emit tables have a fixed size, so they live in static LDS
+// (their offsets fold into the ds_read immediate); only the multi-code
+// kernels reference them, so only those allocate them.
+__shared__ __align__(16) uint32_t s_count_table[df11i::kCountEntries];
+__shared__ __align__(16) uint2 s_emit_table[df11i::kEmitEntries];
+
+// Everything a unit needs from HBM before decoding: the lane's window words
+// (8 bytes + 4-byte halo), its two gap bytes (assembled only when used: any
+// computation on a load result makes the wave wait for it) and the unit's
+// output range.  Loaded one unit ahead so the latency overlaps the previous
+// unit.  u is uniform, so every address is a scalar base plus a lane offset.
+struct UnitInputs {
+    uint32_t w0, w1, w2, gap2;
+    uint64_t p0, p1;
+};
+
+__device__ __forceinline__ void load_unit(const KParams &p, uint64_t u, uint32_t lane, UnitInputs &in) {
+    in.w0 = in.w1 = in.w2 = in.gap2 = 0;
+    const uint64_t w = u * 64 + lane;
+    if (w < p.n_windows) {
+        const uint8_t *sbase = p.stream + 512 * u;
+        const uint2 a = *reinterpret_cast<const uint2 *>(sbase + 8 * lane);
+        in.w0 = a.x;
+        in.w1 = a.y;
+        in.w2 = *reinterpret_cast<const uint32_t *>(sbase + 8 * lane + 8);
+        const uint8_t *gp = p.gaps + 40 * u + ((5 * lane) >> 3);
+        in.gap2 = gp[0] | (static_cast<uint32_t>(gp[1]) << 8);
+    }
+    in.p0 = p.unit_pos[u];
+    in.p1 = p.unit_pos[u + 1];
+}
+
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+constexpr int kPrefetchChunks = 4;  // 8-output chunks of sign/mantissa per lane loaded early
+
+template <bool kDeepGlobal, bool kMulti>
+__device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lut, const uint32_t *ct,
+                                            const uint2 *et, uint16_t *stage, uint32_t lane, uint64_t u,
+                                            const UnitInputs &in, const UnitInputs &next) {
+    // output range of the unit (uniform): staged element k is output base + k
+    const uint64_t q1 = uniform_u64(in.p1), q0 = uniform_u64(in.p0);
+    const uint64_t P1 = q1 < p.n_total ? q1 : p.n_total;
+    const uint64_t P0 = q0 < P1 ? q0 : P1;
+    const uint64_t base = P0 & ~uint64_t{7};
+    const uint64_t span64 = P1 - base;
+    const uint32_t span = span64 < p.stage_elems ? static_cast<uint32_t>(span64) : p.stage_elems;
+    const uint32_t lead = static_cast<uint32_t>(P0 - base);  // staged slots before P0
+    const uint32_t chunks = (span + 7) / 8;
+    const uint8_t *smb = p.sm + base;
+    uint16_t *outb = p.out + base;
+
+    // sign/mantissa bytes of the unit, requested before decoding starts
+    uint2 smv[kPrefetchChunks];
+#pragma unroll
+    for (int k = 0; k < kPrefetchChunks; ++k) {
+        const uint32_t c = lane + 64u * k;
+        smv[k] = c < chunks ? *reinterpret_cast<const uint2 *>(smb + 8u * c) : make_uint2(0, 0);
+    }
+
+    // ---- this lane's window: gap and end (bits of the stream left in it)
+    const uint64_t left = p.total_bits - 4096 * u;  // > 0 for every unit
+    const uint32_t ulim = left < 4096 ? static_cast<uint32_t>(left) : 4096u;
+    const int end = ulim > 64 * lane ? static_cast<int>(ulim - 64 * lane < 64 ? ulim - 64 * lane : 64) : 0;
+    const uint32_t gap2 = ((in.gap2 & 0xFFu) << 8) | (in.gap2 >> 8);  // big-endian 16 bits
+    const uint32_t gap = (gap2 >> (11u - ((5 * lane) & 7))) & 31u;
+    const uint32_t w0 = __builtin_bswap32(in.w0), w1 = __builtin_bswap32(in.w1), w2 = __builtin_bswap32(in.w2);
+
+    // ---- phase 1: count the codes that start in [gap, end)
+    uint32_t cnt;
+    uint32_t h, l, r;
+    start_at(w0, w1, w2, gap, h, l, r);
+    if constexpr (kMulti) {
+        const uint64_t S = ((static_cast<uint64_t>(w0) << 32) | w1) << gap;
+        cnt = count_multi<kDeepGlobal>(lut, ct, p, S, end - static_cast<int>(gap));
+    } else {
+        cnt = count_single<kDeepGlobal>(lut, p, h, l, r, static_cast<int>(gap), end);
+    }
+
+    // ---- wave prefix sum of the counts
+    const uint32_t excl = wave_inclusive_scan(cnt) - cnt;
+
+    // ---- phase 2: decode again, stage (exponent << 7) at the output slot
+    const uint32_t first = lead + excl;
+    const uint32_t room = first < p.stage_elems ? p.stage_elems - first : 0u;
+    const uint32_t n2 = cnt < room ? cnt : room;  // never past this wave's staging
+    if constexpr (kMulti)
+        emit_multi<kDeepGlobal>(lut, et, p, h, l, r, stage + first, n2);
+    else
+        emit_single<kDeepGlobal>(lut, p, h, l, r, stage + first, n2);
+    wave_sync();
+
+    // ---- merge with sign/mantissa and store outputs [lead, span) of the
+    // staging.  All of the unit's outputs are computed before its first
+    // store: vmcnt is in order, so a wait for a load issued before a store
+    // would also wait for that store.
+    auto merge_chunk = [&](uint32_t c, uint2 sm) {
+        const uint4 ev = *reinterpret_cast<const uint4 *>(stage + 8 * c);
+        uint4 o;
+        o.x = merge2(ev.x, sm.x, 0x01010000u);
+        o.y = merge2(ev.y, sm.x, 0x03030202u);
+        o.z = merge2(ev.z, sm.y, 0x01010000u);
+        o.w = merge2(ev.w, sm.y, 0x03030202u);
+        return o;
+    };
+    auto store_chunk = [&](uint32_t c, const uint4 &o) {
+        const uint32_t k0 = 8 * c;
+        if (k0 >= lead && k0 + 8 <= span) {
+            // the output is written once and not read back here: non-temporal
+            typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+            const v4u ov = {o.x, o.y, o.z, o.w};
+            __builtin_nontemporal_store(ov, reinterpret_cast<v4u *>(outb + k0));
+        } else {
+            const uint32_t v[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k)
+                if (k0 + k >= lead && k0 + k < span) outb[k0 + k] = static_cast<uint16_t>(v[k >> 1] >> (16 * (k & 1)));
+        }
+    };
+    uint4 outv[kPrefetchChunks];
+#pragma unroll
+    for (int k = 0; k < kPrefetchChunks; ++k) {
+        const uint32_t c = lane + 64u * k;
+        outv[k] = c < chunks ? merge_chunk(c, smv[k]) : make_uint4(0, 0, 0, 0);
+    }
+    // The next unit's inputs were requested before this unit's sign/mantissa
+    // loads, so they have arrived; taking them here keeps the copy into the
+    // current set (after the stores) from waiting on the stores.
+    asm volatile("" ::"v"(next.w0), "v"(next.w1), "v"(next.w2), "v"(next.gap2), "v"(next.p0), "v"(next.p1));
+#pragma unroll
+    for (int k = 0; k < kPrefetchChunks; ++k) {
+        const uint32_t c = lane + 64u * k;
+        if (c < chunks) store_chunk(c, outv[k]);
+    }
+    for (uint32_t c = lane + 64u * kPrefetchChunks; c < chunks; c += 64)  // units above 2,048 outputs
+        store_chunk(c, merge_chunk(c, *reinterpret_cast<const uint2 *>(smb + 8u * c)));
+    wave_sync();
+}
+
+// Register budget: 8 waves per SIMD (64 VGPRs), the most a CU can hold;
+// the rare kernels that walk sub-tables in global memory get 4 (no spills).
+template <bool kDeepGlobal>
+struct WavesPerEU {
+    static constexpr int value = kDeepGlobal ? 4 : 8;
+};
+
+template <bool kDeepGlobal, bool kMulti>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WavesPerEU<kDeepGlobal>::value)))
+df11_decode_kernel(KParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
-    uint32_t *lut = reinterpret_cast<uint32_t *>(lds);
+    // dynamic LDS: hierarchical tables, then one staging area per wave
     const uint32_t lds_tables = kDeepGlobal ? 1u : p.n_tables;
-    for (uint32_t i = threadIdx.x; i < lds_tables * 256u; i += blockDim.x) lut[i] = p.tables[i];
+    uint32_t *lut = reinterpret_cast<uint32_t *>(lds);
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.tables);
+        uint4 *dst = reinterpret_cast<uint4 *>(lut);
+        for (uint32_t i = threadIdx.x; i < lds_tables * 64u; i += blockDim.x) dst[i] = src[i];
+        if constexpr (kMulti) {
+            const uint4 *msrc = reinterpret_cast<const uint4 *>(p.tables + p.n_tables * 256u);
+            uint4 *cdst = reinterpret_cast<uint4 *>(s_count_table);
+            for (uint32_t i = threadIdx.x; i < df11i::kCountEntries / 4u; i += blockDim.x) cdst[i] = msrc[i];
+            msrc += df11i::kCountEntries / 4u;
+            uint4 *edst = reinterpret_cast<uint4 *>(s_emit_table);
+            for (uint32_t i = threadIdx.x; i < df11i::kEmitEntries / 2u; i += blockDim.x) edst[i] = msrc[i];
+        }
+    }
     __syncthreads();
 
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = threadIdx.x >> 6;
-    const uint32_t waves = blockDim.x >> 6;
+    // wave index and wave count are uniform: keep unit indices in scalar registers
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
     uint16_t *stage = reinterpret_cast<uint16_t *>(lds + lds_tables * 1024u) + wave * p.stage_elems;
-    const uint64_t n_groups = (p.n_units + waves - 1) / waves;
+    const uint64_t stride = uint64_t{gridDim.x} * waves;
 
-    for (uint64_t grp = blockIdx.x; grp < n_groups; grp += gridDim.x) {
-        const uint64_t u = grp * waves + wave;
-        if (u >= p.n_units) continue;  // uniform across the wave
-
-        // ---- window words, gap and end of this lane's window
-        const uint64_t w = u * 64 + lane;
-        uint32_t w0 = 0, w1 = 0, w2 = 0, gap = 0;
-        int end = 0;
-        if (w < p.n_windows) {
-            const uint2 a = *reinterpret_cast<const uint2 *>(p.stream + 8 * w);
-            const uint32_t c = *reinterpret_cast<const uint32_t *>(p.stream + 8 * w + 8);
-            w0 = __builtin_bswap32(a.x);
-            w1 = __builtin_bswap32(a.y);
-            w2 = __builtin_bswap32(c);
-            const uint64_t gb = 5 * w;
-            const uint8_t *gp = p.gaps + (gb >> 3);
-            const uint32_t two = (static_cast<uint32_t>(gp[0]) << 8) | gp[1];
-            gap = (two >> (11u - static_cast<uint32_t>(gb & 7))) & 31u;
-            const uint64_t left = p.total_bits - 64 * w;
-            end = left < 64 ? static_cast<int>(left) : 64;
-        }
-        uint64_t P1 = p.unit_pos[u + 1];
-        uint64_t P0 = p.unit_pos[u];
-        P1 = P1 < p.n_total ? P1 : p.n_total;
-        P0 = P0 < P1 ? P0 : P1;
-
-        // ---- phase 1: count the codes that start in [gap, end)
-        uint32_t h, l, r;
-        start_at(w0, w1, w2, gap, h, l, r);
-        int pos = static_cast<int>(gap);
-        uint32_t cnt = 0;
-        while (pos < end) {
-            const uint32_t e = lookup<kDeepGlobal>(lut, p.tables, p.n_tables, h);
-            consume(e, h, l, r);
-            pos += static_cast<int>((e >> 8) & 31u) + 1;
-            ++cnt;
-        }
-
-        // ---- wave prefix sum of the counts
-        uint32_t incl = cnt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t t = __shfl_up(incl, d, 64);
-            if (lane >= static_cast<uint32_t>(d)) incl += t;
-        }
-        const uint32_t excl = incl - cnt;
-
-        // ---- phase 2: decode again, stage (exponent << 7) at the output slot
-        const uint64_t base = P0 & ~uint64_t{7};  // stage[k] holds output base + k
-        const uint32_t first = static_cast<uint32_t>(P0 - base) + excl;
-        const uint32_t room = first < p.stage_elems ? p.stage_elems - first : 0u;
-        const uint32_t n2 = cnt < room ? cnt : room;  // never past this wave's staging
-        start_at(w0, w1, w2, gap, h, l, r);
-        for (uint32_t j = 0; j < n2; ++j) {
-            const uint32_t e = lookup<kDeepGlobal>(lut, p.tables, p.n_tables, h);
-            consume(e, h, l, r);
-            stage[first + j] = static_cast<uint16_t>(e >> 16);
-        }
-        wave_sync();
-
-        // ---- merge with sign/mantissa and store [P0, P1)
-        uint64_t span = P1 - base;
-        span = span < p.stage_elems ? span : p.stage_elems;
-        const uint64_t stop = base + span;
-        const uint32_t chunks = static_cast<uint32_t>((span + 7) / 8);
-        for (uint32_t c = lane; c < chunks; c += 64) {
-            const uint64_t g0 = base + 8ull * c;
-            const uint4 ev = *reinterpret_cast<const uint4 *>(stage + 8 * c);
-            const uint2 s = *reinterpret_cast<const uint2 *>(p.sm + g0);
-            uint4 o;
-            o.x = merge2(ev.x, s.x, 0x01010000u);
-            o.y = merge2(ev.y, s.x, 0x03030202u);
-            o.z = merge2(ev.z, s.y, 0x01010000u);
-            o.w = merge2(ev.w, s.y, 0x03030202u);
-            if (g0 >= P0 && g0 + 8 <= stop) {
-                *reinterpret_cast<uint4 *>(p.out + g0) = o;
-            } else {
-                const uint32_t v[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const uint64_t g = g0 + k;
-                    if (g >= P0 && g < stop) p.out[g] = static_cast<uint16_t>(v[k >> 1] >> (16 * (k & 1)));
-                }
-            }
-        }
-        wave_sync();
+    uint64_t u = uint64_t{blockIdx.x} * waves + wave;
+    UnitInputs cur;
+    if (u < p.n_units) load_unit(p, u, lane, cur);
+    while (u < p.n_units) {  // uniform across the wave
+        UnitInputs nxt = {0, 0, 0, 0, 0, 0};
+        if (u + stride < p.n_units) load_unit(p, u + stride, lane, nxt);
+        decode_unit<kDeepGlobal, kMulti>(p, lut, s_count_table, s_emit_table, stage, lane, u, cur, nxt);
+        cur = nxt;  // waits for the next unit's inputs, requested a whole unit ago
+        u += stride;
     }
 }
 
@@ -210,24 +401,39 @@ thread_local int32_t g_last_hip_error = 0;
 
 struct DeviceInfo {
     int cus = 0;
+    int lds_per_group = 0;
 };
 
 std::mutex g_mu;
 DeviceInfo g_dev[64];
 
-int cu_count(int dev) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    if (dev < 0 || dev >= 64) return 256;
-    if (!g_dev[dev].cus) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-            (void)hipGetLastError();
-            v = 256;
-        }
-        if (v <= 0) v = 256;
-        g_dev[dev].cus = v;
+int device_attr(hipDeviceAttribute_t a, int dev, int fallback) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, a, dev) != hipSuccess) {
+        (void)hipGetLastError();  // our own failed query: do not leave it to the caller
+        return fallback;
     }
-    return g_dev[dev].cus;
+    return v > 0 ? v : fallback;
+}
+
+DeviceInfo device_info(int dev) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (dev < 0 || dev >= 64) return DeviceInfo{256, 65536};
+    if (!g_dev[dev].cus) {
+        g_dev[dev].cus = device_attr(hipDeviceAttributeMultiprocessorCount, dev, 256);
+        g_dev[dev].lds_per_group = device_attr(hipDeviceAttributeMaxSharedMemoryPerBlock, dev, 65536);
+    }
+    return g_dev[dev];
+}
+
+int occupancy(const void *fn, uint32_t waves, uint32_t lds_bytes) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, static_cast<int>(64 * waves), lds_bytes) !=
+        hipSuccess) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    return per_cu > 0 ? per_cu : 0;
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -265,15 +471,47 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
                                             const df11_launch *launch) {
     df11_status rc = check_block(blk, out_bf16, out_capacity);
     if (rc != DF11_OK || blk->n_total == 0) return rc;
-    uint32_t waves = (launch && launch->waves_per_group) ? launch->waves_per_group : 4u;
-    if (waves != 1 && waves != 2 && waves != 4 && waves != 8 && waves != 16) return DF11_E_INVALID_ARG;
+    const uint32_t variant = (launch && launch->variant) ? launch->variant : DF11_VARIANT_MULTI;
+    if (variant != DF11_VARIANT_SINGLE && variant != DF11_VARIANT_MULTI) return DF11_E_INVALID_ARG;
+    const bool multi = variant == DF11_VARIANT_MULTI;
+    if (multi && blk->tables_bytes < df11i::tables_bytes_for(blk->n_tables)) return DF11_E_INVALID_ARG;
+    const uint32_t asked = launch ? launch->waves_per_group : 0u;
+    if (asked != 0 && asked != 1 && asked != 2 && asked != 4 && asked != 8 && asked != 16)
+        return DF11_E_INVALID_ARG;
 
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        dev = 0;
+    }
+    const DeviceInfo info = device_info(dev);
     const bool deep_global = blk->n_tables > kLdsTableMax;
+    const void *fn;
+    if (multi)
+        fn = deep_global ? reinterpret_cast<const void *>(&df11_decode_kernel<true, true>)
+                         : reinterpret_cast<const void *>(&df11_decode_kernel<false, true>);
+    else
+        fn = deep_global ? reinterpret_cast<const void *>(&df11_decode_kernel<true, false>)
+                         : reinterpret_cast<const void *>(&df11_decode_kernel<false, false>);
+
+    // LDS per workgroup: static (count and emit tables) + hierarchical tables
+    // + one staging area per wave; it bounds how many waves are resident.
     const uint32_t lds_tables = deep_global ? 1u : blk->n_tables;
+    const uint32_t fixed_static = multi ? static_cast<uint32_t>(df11i::kMultiTableBytes) : 0u;
     const uint32_t stage_elems = static_cast<uint32_t>((blk->max_unit_count + 7 + 7) / 8 * 8);
-    while (waves > 1 && lds_tables * 1024u + waves * stage_elems * 2u > kMaxLdsBytes) waves >>= 1;
-    const uint32_t lds_bytes = lds_tables * 1024u + waves * stage_elems * 2u;
-    if (lds_bytes > kMaxLdsBytes) return DF11_E_UNSUPPORTED;
+    auto lds_for = [&](uint32_t w) { return lds_tables * 1024u + w * stage_elems * 2u; };
+    uint32_t waves = 0, per_cu = 0;
+    for (uint32_t w = 16; w >= 1; w >>= 1) {  // the geometry with the most resident waves
+        if (asked && w != asked) continue;
+        if (fixed_static + lds_for(w) > static_cast<uint32_t>(info.lds_per_group)) continue;
+        const uint32_t occ = static_cast<uint32_t>(occupancy(fn, w, lds_for(w)));
+        if (occ && (!waves || occ * w > per_cu * waves)) {
+            waves = w;
+            per_cu = occ;
+        }
+    }
+    if (!waves) return DF11_E_UNSUPPORTED;
+    const uint32_t lds_bytes = lds_for(waves);
 
     KParams p;
     p.tables = static_cast<const uint32_t *>(blk->tables);
@@ -289,19 +527,11 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     p.n_tables = blk->n_tables;
     p.stage_elems = stage_elems;
 
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    const void *fn = deep_global ? reinterpret_cast<const void *>(&df11_decode_kernel<true>)
-                                 : reinterpret_cast<const void *>(&df11_decode_kernel<false>);
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, static_cast<int>(64 * waves),
-                                                     lds_bytes) != hipSuccess) {
-        (void)hipGetLastError();  // our own failed query: do not leave it to the caller
-        per_cu = 1;
-    }
-    if (per_cu <= 0) per_cu = 1;
+    // Several workgroups per resident slot (each then loops over fewer units)
+    // stream better than one persistent wave of workgroups.
+    const uint32_t over = (launch && launch->oversubscribe) ? launch->oversubscribe : kDefaultOversubscribe;
     const uint64_t groups = (blk->n_units + waves - 1) / waves;
-    uint64_t grid = std::min<uint64_t>(groups, uint64_t(cu_count(dev)) * uint64_t(per_cu));
+    uint64_t grid = std::min<uint64_t>(groups, uint64_t(info.cus) * uint64_t(per_cu) * over);
     if (launch && launch->max_groups) grid = std::min<uint64_t>(grid, launch->max_groups);
     grid = std::max<uint64_t>(grid, 1);
 

@@ -256,7 +256,7 @@ extern "C" df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_
     s.stream_bytes = 512 * n_units + 16;
     s.sign_mant_bytes = round_up(N, 16);
     s.gaps_bytes = 40 * n_units + 8;
-    s.tables_bytes = uint64_t{n_tables} * 1024;
+    s.tables_bytes = df11i::tables_bytes_for(n_tables);
     uint64_t off = 256;  // reserved header
     auto place = [&](uint64_t bytes) {
         const uint64_t at = off;

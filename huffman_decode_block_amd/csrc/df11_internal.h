@@ -26,10 +26,31 @@ constexpr uint32_t pointer_entry(uint32_t table) {
 // corrupt lengths): a 1-bit leaf of exponent 0, so a decoder always advances.
 constexpr uint32_t kFillerEntry = leaf_entry(0, 1);
 
-// Builds the decode tables for the 256 code lengths into dst (entries), or
-// only counts them when dst is null.  Returns DF11_OK, DF11_E_FORMAT or
-// DF11_E_BUFFER_TOO_SMALL.
-df11_status build_tables(const uint8_t code_len[256], uint32_t *dst, uint64_t dst_entries,
+// Multi-code tables, placed after the hierarchical ones (all derived from the
+// same canonical code):
+//   count table, indexed by the next kCountBits stream bits, 32-bit entries:
+//     bits 30..20 = start mask (bit 20+j set when a code starts at offset j and
+//     ends inside the index bits), bits 5..0 = bits taken by those complete
+//     codes (t, also the shift amount of a 64-bit shift), other bits 0; an
+//     entry of 0 means the first code is longer than kCountBits.
+//   emit table, indexed by the next kEmitBits bits, 64-bit entries: the first
+//     n = min(3, complete codes) exponents as 16-bit (exponent << 7) values v0,
+//     v1 in the low word and v2 in bits 63..48; bits 43..42 = n; bits 41..37 =
+//     (32 - length of the first code) & 31; bits 36..32 = (32 - t) & 31 with t
+//     the bits of the n codes; n = 0 means the first code is longer than
+//     kEmitBits.
+constexpr uint32_t kCountBits = 11;
+constexpr uint32_t kEmitBits = 10;
+constexpr uint32_t kCountEntries = 1u << kCountBits;
+constexpr uint32_t kEmitEntries = 1u << kEmitBits;
+constexpr uint64_t kMultiTableBytes = uint64_t{kCountEntries} * 4 + uint64_t{kEmitEntries} * 8;
+constexpr uint64_t tables_bytes_for(uint32_t n_hier) { return uint64_t{n_hier} * 1024 + kMultiTableBytes; }
+
+// Builds the decode tables for the 256 code lengths into dst (32-bit words:
+// the hierarchical tables, then the count and emit tables), or only counts
+// the hierarchical tables when dst is null.  Returns DF11_OK, DF11_E_FORMAT
+// or DF11_E_BUFFER_TOO_SMALL.
+df11_status build_tables(const uint8_t code_len[256], uint32_t *dst, uint64_t dst_words,
                          uint32_t *n_tables);
 
 // Canonical codewords for the lengths (right aligned).  Returns false if the

@@ -40,7 +40,21 @@ bool canonical_codes(const uint8_t code_len[256], uint32_t code[256]) {
     return true;
 }
 
-df11_status build_tables(const uint8_t code_len[256], uint32_t *dst, uint64_t dst_entries,
+namespace {
+
+// One code from a left-aligned 32-bit window, through the hierarchical tables.
+uint32_t walk(const std::vector<uint32_t> &t, uint32_t window) {
+    uint32_t e = t[window >> 24];
+    for (int lvl = 1; lvl < 4 && (e & kPointerFlag); ++lvl)
+        e = t[((e >> 16) & 0x7FFFu) * 256 + ((window >> (24 - 8 * lvl)) & 0xFFu)];
+    return e;
+}
+
+uint32_t entry_length(uint32_t e) { return ((e >> 8) & 31u) + 1; }
+
+}  // namespace
+
+df11_status build_tables(const uint8_t code_len[256], uint32_t *dst, uint64_t dst_words,
                          uint32_t *n_tables) {
     uint32_t code[256];
     if (!canonical_codes(code_len, code)) return DF11_E_FORMAT;
@@ -84,9 +98,43 @@ df11_status build_tables(const uint8_t code_len[256], uint32_t *dst, uint64_t ds
         if (v == kUnset) v = kFillerEntry;
     const uint32_t nt = static_cast<uint32_t>(t.size() / 256);
     if (n_tables) *n_tables = nt;
-    if (dst) {
-        if (dst_entries < t.size()) return DF11_E_BUFFER_TOO_SMALL;
-        std::copy(t.begin(), t.end(), dst);
+    if (!dst) return DF11_OK;
+    if (dst_words < tables_bytes_for(nt) / 4) return DF11_E_BUFFER_TOO_SMALL;
+    std::copy(t.begin(), t.end(), dst);
+
+    // count table: every code that starts and ends inside the index bits
+    uint32_t *count = dst + t.size();
+    for (uint32_t p = 0; p < kCountEntries; ++p) {
+        uint32_t pos = 0, mask = 0;
+        while (pos < kCountBits) {
+            const uint32_t window = (p << (32 - kCountBits)) << pos;
+            const uint32_t l = entry_length(walk(t, window));
+            if (l > kCountBits - pos) break;
+            mask |= 1u << pos;
+            pos += l;
+        }
+        count[p] = pos ? (mask << 20) | pos : 0u;
+    }
+    // emit table: up to three codes that end inside the index bits
+    uint32_t *emit = count + kCountEntries;
+    for (uint32_t p = 0; p < kEmitEntries; ++p) {
+        uint32_t pos = 0, n = 0, first_len = 0, v[3] = {0, 0, 0};
+        while (n < 3 && pos < kEmitBits) {
+            const uint32_t window = (p << (32 - kEmitBits)) << pos;
+            const uint32_t e = walk(t, window);
+            const uint32_t l = entry_length(e);
+            if (l > kEmitBits - pos) break;
+            v[n] = e >> 16;  // exponent << 7
+            if (n == 0) first_len = l;
+            pos += l;
+            n += 1;
+        }
+        const uint32_t lo = n ? (v[0] | (v[1] << 16)) : 0u;
+        const uint32_t hi = n ? ((v[2] << 16) | (n << 10) | (((32u - first_len) & 31u) << 5) |
+                                 ((32u - pos) & 31u))
+                              : 0u;
+        emit[2 * p] = lo;
+        emit[2 * p + 1] = hi;
     }
     return DF11_OK;
 }
@@ -99,7 +147,7 @@ extern "C" df11_status df11_tables_size(const uint8_t code_len[256], uint64_t *b
     uint32_t nt = 0;
     df11_status rc = df11i::build_tables(code_len, nullptr, 0, &nt);
     if (rc != DF11_OK) return rc;
-    *bytes = static_cast<uint64_t>(nt) * 256u * sizeof(uint32_t);
+    *bytes = df11i::tables_bytes_for(nt);
     if (n_tables) *n_tables = nt;
     return DF11_OK;
 }

@@ -139,9 +139,11 @@ df11_status df11_validate(const df11_sections *s);
 /* Decode tables for the GPU kernel, derived from the 256 code lengths: a
  * hierarchy of 256-entry tables indexed by 8 stream bits each (the pages'
  * compact LUTs, section "Decodage fonde sur des LUT hierarchiques"), with
- * 32-bit entries.  df11_tables_size reports the bytes needed and the table
- * count; df11_build_tables writes them to dst (host memory, dst_bytes at
- * least that size).  Errors: DF11_E_INVALID_ARG, DF11_E_FORMAT (lengths do
+ * 32-bit entries, followed by a 2048-entry count table and a 1024-entry emit
+ * table that resolve several codes per lookup (16 KiB).  df11_tables_size
+ * reports the bytes needed and the number of hierarchical tables;
+ * df11_build_tables writes them to dst (host memory, dst_bytes at least that
+ * size).  Errors: DF11_E_INVALID_ARG, DF11_E_FORMAT (lengths do
  * not form a prefix code of at most 32 bits), DF11_E_BUFFER_TOO_SMALL. */
 df11_status df11_tables_size(const uint8_t code_len[256], uint64_t *bytes, uint32_t *n_tables);
 df11_status df11_build_tables(const uint8_t code_len[256], void *dst, uint64_t dst_bytes);
@@ -180,10 +182,23 @@ df11_status df11_device_block_from_blob(const df11_sections *s, const void *devi
 df11_status df11_decode_block(const df11_device_block *blk, uint16_t *out_bf16,
                               uint64_t out_capacity, void *hip_stream);
 
+/* Kernel variants (the output never depends on the choice):
+ *  DF11_VARIANT_SINGLE: one code per table lookup in both phases, 8-bit
+ *    indexed hierarchical tables only (the pages' kernel design);
+ *  DF11_VARIANT_MULTI: phase 1 takes every code that ends in the next 11 bits
+ *    per lookup (count table), phase 2 up to three codes in the next 10 bits
+ *    (emit table); codes longer than that and the last one or two codes of a
+ *    window go through the hierarchical tables.  The default. */
+#define DF11_VARIANT_SINGLE 1u
+#define DF11_VARIANT_MULTI 2u
+
 /* Launch geometry for df11_decode_block_ex (0 = automatic). */
 typedef struct df11_launch {
     uint32_t waves_per_group;  /* 64-lane waves per workgroup: 1, 2, 4, 8 or 16 */
-    uint32_t max_groups;       /* cap on the grid size (persistent workgroups) */
+    uint32_t max_groups;       /* cap on the grid size */
+    uint32_t variant;          /* DF11_VARIANT_*, 0 = DF11_VARIANT_MULTI */
+    uint32_t oversubscribe;    /* workgroups launched per resident workgroup slot
+                                  (1 = persistent grid); 0 = automatic */
 } df11_launch;
 
 /* df11_decode_block with an explicit launch geometry; the output does not

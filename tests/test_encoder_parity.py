@@ -98,7 +98,7 @@ def test_tables_decode_every_oracle_codeword(case):
     codes = oracle.canonical_codes(ln)
     t = hdb.df11_build_tables(ln.astype(np.uint8)).view(np.uint32)
     nb, nt = hdb.df11_tables_size(ln.astype(np.uint8))
-    assert nb == t.nbytes == nt * 1024
+    assert nb == t.nbytes == nt * 1024 + 2048 * 4 + 1024 * 8
     for e in np.nonzero(ln)[0]:
         bits = format(int(codes[e]), "0{}b".format(int(ln[e])))
         # any continuation bits must not change the result
@@ -144,3 +144,64 @@ def test_validate_detects_corruption(what):
     elif what == "max_unit_count":
         s.raw.max_unit_count += 1
     assert hdb.df11_validate(s) == hdb.DF11_E_FORMAT
+
+
+def _greedy(bits, codes_by_bits, complete, limit):
+    """Codes that start and end inside `bits` (a '0'/'1' string), greedily,
+    at most `limit` of them: list of (exponent, length).  Bits that begin no
+    codeword of an incomplete code read as a 1-bit code of exponent 0 (the
+    tables' documented filler)."""
+    out, pos = [], 0
+    while pos < len(bits) and len(out) < limit:
+        hit = None
+        for L in range(1, len(bits) - pos + 1):
+            e = codes_by_bits.get(bits[pos:pos + L])
+            if e is not None:
+                hit = (e, L)
+                break
+        if hit is None:
+            if complete:
+                break  # the codeword runs past the index bits
+            hit = (0, 1)
+        out.append(hit)
+        pos += hit[1]
+    return out
+
+
+@pytest.mark.parametrize("case", ["c1", "fib34", "many_subtables", "all_patterns", "single", "skew"])
+def test_count_and_emit_tables(case):
+    x = {"c1": lambda: di.generate("C1"), "fib34": lambda: di.fibonacci_exponents(),
+         "many_subtables": lambda: di.many_subtables(), "all_patterns": lambda: di.all_bf16_patterns(),
+         "single": lambda: di.single_exponent(10, 9, 1), "skew": lambda: di.skewed(100_000, 90, 1.6, 5)}[case]()
+    ln = oracle.code_lengths(oracle.histogram(x))
+    codes = oracle.canonical_codes(ln)
+    by_bits = {format(int(codes[e]), "0{}b".format(int(ln[e]))): int(e) for e in np.nonzero(ln)[0]}
+    complete = len(by_bits) > 1
+    t = hdb.df11_build_tables(ln.astype(np.uint8)).view(np.uint32)
+    _, nt = hdb.df11_tables_size(ln.astype(np.uint8))
+    count = t[nt * 256: nt * 256 + 2048]
+    emit = t[nt * 256 + 2048:].reshape(1024, 2)
+    for p in range(2048):
+        got = _greedy(format(p, "011b"), by_bits, complete, 11)
+        tb = sum(L for _, L in got)
+        mask = 0
+        pos = 0
+        for _, L in got:
+            mask |= 1 << pos
+            pos += L
+        want = (mask << 20) | tb if tb else 0
+        assert int(count[p]) == want, (p, hex(int(count[p])), hex(want))
+    for p in range(1024):
+        got = _greedy(format(p, "010b"), by_bits, complete, 3)
+        lo, hi = int(emit[p, 0]), int(emit[p, 1])
+        n = (hi >> 10) & 3
+        assert n == len(got)
+        if not got:
+            assert lo == 0 and hi == 0
+            continue
+        vals = [e << 7 for e, _ in got] + [0, 0]
+        tb = sum(L for _, L in got)
+        assert lo == vals[0] | (vals[1] << 16)
+        assert hi >> 16 == vals[2]
+        assert hi & 31 == (32 - tb) & 31
+        assert (hi >> 5) & 31 == (32 - got[0][1]) & 31

@@ -50,17 +50,22 @@ def decode_guarded(torch, blk, n, poison, launch=None, stream=None):
     return h[GUARD:GUARD + n].copy()
 
 
-def check_oracle_sections(torch, x, name):
+def check_oracle_sections(torch, x, name, variants=(0,)):
     o = oracle.encode(x)
     expect = oracle.decode(o)
     np.testing.assert_array_equal(expect, x)
     blk = hdb.DeviceBlock.from_parts(code_len=o.code_len, stream=o.stream, sign_mant=o.sign_mant,
                                      gaps=o.gaps, unit_pos=o.unit_pos, n_total=o.n,
                                      total_bits=o.total_bits)
-    for poison in (0x5A5A, -1):
-        say(f"{name}: oracle sections n={x.size} max_len={o.max_len} poison={poison & 0xFFFF:#x}")
-        y = decode_guarded(torch, blk, x.size, poison)
-        np.testing.assert_array_equal(y, expect)
+    for variant in variants:
+        for poison in (0x5A5A, -1):
+            say(f"{name}: oracle sections n={x.size} max_len={o.max_len} variant={variant} "
+                f"poison={poison & 0xFFFF:#x}")
+            y = decode_guarded(torch, blk, x.size, poison, launch=(0, 0, variant))
+            np.testing.assert_array_equal(y, expect)
+
+
+VARIANTS = [hdb.DF11_VARIANT_SINGLE, hdb.DF11_VARIANT_MULTI]
 
 
 def check_library_blob(torch, x, name, mats=None, launch=None):
@@ -93,23 +98,24 @@ EDGE = {
 @pytest.mark.parametrize("name", ["v1_mixed_small", "v3_single_exponent", "v5_straddle_window",
                                   "v6_last_window_without_start"])
 def test_golden_vectors(torch, name):
-    check_oracle_sections(torch, np.array(load_golden(name)["x"], dtype=np.uint16), name)
+    check_oracle_sections(torch, np.array(load_golden(name)["x"], dtype=np.uint16), name, VARIANTS)
 
 
 @pytest.mark.parametrize("n", [1, 2, 7, 63, 64, 65, 255, 4095, 4096, 4097, 8191, 262_143,
                                262_145, 1_000_003])
 def test_ragged_sizes(torch, n):
-    check_oracle_sections(torch, di.random_normal(n, 0.02, 500 + n), f"ragged_{n}")
+    check_oracle_sections(torch, di.random_normal(n, 0.02, 500 + n), f"ragged_{n}", VARIANTS)
 
 
 @pytest.mark.parametrize("case", sorted(EDGE))
 def test_edge_inputs_oracle_sections(torch, case):
-    check_oracle_sections(torch, EDGE[case](), case)
+    check_oracle_sections(torch, EDGE[case](), case, VARIANTS)
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("case", sorted(EDGE))
-def test_edge_inputs_library_blob(torch, case):
-    check_library_blob(torch, EDGE[case](), case)
+def test_edge_inputs_library_blob(torch, case, variant):
+    check_library_blob(torch, EDGE[case](), case, launch=(0, 0, variant))
 
 
 def test_empty_block_is_a_noop(torch):
@@ -121,17 +127,20 @@ def test_empty_block_is_a_noop(torch):
     assert (buf.cpu() == 7).all()
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("waves", [1, 2, 4, 8, 16])
-@pytest.mark.parametrize("max_groups", [0, 1, 7])
-def test_launch_geometry_does_not_change_the_output(torch, waves, max_groups):
+@pytest.mark.parametrize("max_groups,over", [(0, 0), (1, 0), (7, 0), (0, 1), (0, 64)])
+def test_launch_geometry_does_not_change_the_output(torch, waves, max_groups, over, variant):
     x = di.generate("C1") if max_groups == 1 else di.random_normal(3_000_000, 0.02, 77)
-    check_library_blob(torch, x, f"geometry_w{waves}_g{max_groups}", launch=(waves, max_groups))
+    check_library_blob(torch, x, f"geometry_w{waves}_g{max_groups}_o{over}_v{variant}",
+                       launch=(waves, max_groups, variant, over))
 
 
 def test_workload_c2(torch):
     x = di.generate("C2")
-    check_oracle_sections(torch, x, "C2")
-    check_library_blob(torch, x, "C2")
+    check_oracle_sections(torch, x, "C2", VARIANTS)
+    for v in VARIANTS:
+        check_library_blob(torch, x, "C2", launch=(0, 0, v))
 
 
 def test_side_stream(torch):
@@ -160,7 +169,7 @@ def test_device_side_errors(torch):
     assert ei.value.status == hdb.DF11_E_INVALID_ARG
 
 
-def _full_block(torch, key):
+def _full_block(torch, key, variants=(0,)):
     say(f"{key}: generating")
     x = di.generate(key)
     mats = di.split(key, x)
@@ -170,17 +179,23 @@ def _full_block(torch, key):
     assert hdb.df11_validate(s) == hdb.DF11_OK
     blk = hdb.DeviceBlock.from_encoded(enc)
     out = torch.empty(x.size, dtype=torch.bfloat16, device="cuda")
-    say(f"{key}: decoding units={s.n_units} tables={s.n_tables} max_len={s.max_code_len}")
-    hdb.df11_decode_block(blk, out=out)
-    torch.cuda.synchronize()
     xd = torch.from_numpy(x.view(np.int16)).to("cuda")
-    ident = bool(torch.equal(out.view(torch.int16), xd))
+    ref = None
+    for variant in variants:
+        out.view(torch.int16).fill_(0x5A5A)
+        say(f"{key}: decoding units={s.n_units} tables={s.n_tables} max_len={s.max_code_len} "
+            f"variant={variant}")
+        hdb.df11_decode_block(blk, out=out, launch=(0, 0, variant))
+        torch.cuda.synchronize()
+        ident = bool(torch.equal(out.view(torch.int16), xd))
+        say(f"{key}: identity {ident}; oracle decode of every unit")
+        y = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        if ref is None:
+            ref = oracle.decode_units(oracle_view(s), threads=16)
+        np.testing.assert_array_equal(y, ref)
+        assert ident
+        del y
     del xd
-    say(f"{key}: identity {ident}; oracle decode of every unit")
-    y = out.view(torch.int16).cpu().numpy().view(np.uint16)
-    ref = oracle.decode_units(oracle_view(s), threads=16)
-    np.testing.assert_array_equal(y, ref)
-    assert ident
     # per-matrix views
     wl = di.WORKLOADS[key]
     views = hdb.matrix_views(out, blk, [(m.rows, m.cols) for m in wl.mats])
@@ -190,7 +205,7 @@ def _full_block(torch, key):
 
 
 def test_workload_c3_full(torch):
-    x, enc = _full_block(torch, "C3")
+    x, enc = _full_block(torch, "C3", VARIANTS)
     # the library's sections equal the oracle's own encoding at full size
     say("C3: oracle encode for section parity")
     o = oracle.encode(x)
@@ -205,4 +220,4 @@ def test_workload_c4_full(torch):
 
 
 def test_workload_c5_full(torch):
-    _full_block(torch, "C5")
+    _full_block(torch, "C5", VARIANTS)
