@@ -178,30 +178,35 @@ __device__ __forceinline__ void emit_single(const uint32_t *lut, const KParams &
     for (uint32_t j = 0; j < n; ++j) dst[j] = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
 }
 
-// Phase 2 with the emit table: up to three codes per lookup.  While at least
-// three values remain, all three slots are written (slots past the codes
-// actually taken belong to this lane and are overwritten next); the last
-// one or two values go through the single-code path.
+// Phase 2 with the emit table: up to four codes per lookup.  While at least
+// four values remain, the whole 8-byte entry is stored (slots past the codes
+// actually taken belong to this lane and are overwritten next); in the last
+// step only the remaining slots are written.
 template <bool kDeepGlobal>
 __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et, const KParams &p, uint32_t h,
-                                           uint32_t l, uint32_t r, uint16_t *dst, uint32_t n) {
-    while (n >= 3) {
+                                           uint32_t l, uint32_t r, uint16_t *dst, uint32_t left) {
+    typedef uint64_t u64_a2 __attribute__((aligned(2)));  // staging slots are 2-byte aligned
+    while (left > 0) {
         const uint64_t ev = *reinterpret_cast<const uint64_t *>(et + (h >> (32 - df11i::kEmitBits)));
-        const uint2 e = make_uint2(static_cast<uint32_t>(ev), static_cast<uint32_t>(ev >> 32));
-        const uint32_t k = (e.y >> 10) & 3u;
-        if (__builtin_expect(k == 0u, 0)) {  // first code longer than the index
+        const uint32_t lo = static_cast<uint32_t>(ev);
+        const uint32_t n = (lo >> 16) & 7u;
+        if (__builtin_expect(n == 0u, 0)) {  // first code longer than the index
             *dst++ = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
-            --n;
+            --left;
             continue;
         }
-        dst[0] = static_cast<uint16_t>(e.x);
-        dst[1] = static_cast<uint16_t>(e.x >> 16);
-        dst[2] = static_cast<uint16_t>(e.y >> 16);
-        consume(e.y, h, l, r);
-        dst += k;
-        n -= k;
+        if (left >= df11i::kEmitCodes) {
+            *reinterpret_cast<u64_a2 *>(dst) = ev;
+        } else {
+            dst[0] = static_cast<uint16_t>(lo);
+            if (left > 1) dst[1] = static_cast<uint16_t>(lo >> 16);
+            if (left > 2) dst[2] = static_cast<uint16_t>(ev >> 32);
+            if (n >= left) break;  // the last values of this window are written
+        }
+        consume(lo, h, l, r);
+        dst += n;
+        left -= n;
     }
-    for (; n > 0; --n) *dst++ = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
 }
 
 // The count and emit tables have a fixed size, so they live in static LDS

@@ -29,18 +29,21 @@ constexpr uint32_t kFillerEntry = leaf_entry(0, 1);
 // Multi-code tables, placed after the hierarchical ones (all derived from the
 // same canonical code):
 //   count table, indexed by the next kCountBits stream bits, 32-bit entries:
-//     bits 30..20 = start mask (bit 20+j set when a code starts at offset j and
+//     bits 29..20 = start mask (bit 20+j set when a code starts at offset j and
 //     ends inside the index bits), bits 5..0 = bits taken by those complete
 //     codes (t, also the shift amount of a 64-bit shift), other bits 0; an
 //     entry of 0 means the first code is longer than kCountBits.
-//   emit table, indexed by the next kEmitBits bits, 64-bit entries: the first
-//     n = min(3, complete codes) exponents as 16-bit (exponent << 7) values v0,
-//     v1 in the low word and v2 in bits 63..48; bits 43..42 = n; bits 41..37 =
-//     (32 - length of the first code) & 31; bits 36..32 = (32 - t) & 31 with t
-//     the bits of the n codes; n = 0 means the first code is longer than
-//     kEmitBits.
-constexpr uint32_t kCountBits = 11;
-constexpr uint32_t kEmitBits = 10;
+//   emit table, indexed by the next kEmitBits bits, 64-bit entries holding
+//     four 16-bit slots, slot k = (exponent_k << 7) | field_k, for the first
+//     n = min(4, complete codes) codes.  An exponent shifted into its BF16
+//     position leaves bits 6..0 free, which carry: field_0 = (32 - t) & 31
+//     with t the bits of the n codes (the alignbit amount), field_1 = n.
+//     n = 0 means the first code is longer than kEmitBits.  Slots past n are
+//     0.  The whole entry can be written to a staging buffer as is: a reader
+//     takes only bits 14..7 of a slot.
+constexpr uint32_t kCountBits = 10;
+constexpr uint32_t kEmitBits = 11;
+constexpr uint32_t kEmitCodes = 4;
 constexpr uint32_t kCountEntries = 1u << kCountBits;
 constexpr uint32_t kEmitEntries = 1u << kEmitBits;
 constexpr uint64_t kMultiTableBytes = uint64_t{kCountEntries} * 4 + uint64_t{kEmitEntries} * 8;

@@ -115,26 +115,25 @@ df11_status build_tables(const uint8_t code_len[256], uint32_t *dst, uint64_t ds
         }
         count[p] = pos ? (mask << 20) | pos : 0u;
     }
-    // emit table: up to three codes that end inside the index bits
+    // emit table: up to four codes that end inside the index bits
     uint32_t *emit = count + kCountEntries;
     for (uint32_t p = 0; p < kEmitEntries; ++p) {
-        uint32_t pos = 0, n = 0, first_len = 0, v[3] = {0, 0, 0};
-        while (n < 3 && pos < kEmitBits) {
+        uint32_t pos = 0, n = 0, slot[kEmitCodes] = {0, 0, 0, 0};
+        while (n < kEmitCodes && pos < kEmitBits) {
             const uint32_t window = (p << (32 - kEmitBits)) << pos;
             const uint32_t e = walk(t, window);
             const uint32_t l = entry_length(e);
             if (l > kEmitBits - pos) break;
-            v[n] = e >> 16;  // exponent << 7
-            if (n == 0) first_len = l;
+            slot[n] = e >> 16;  // exponent << 7
             pos += l;
             n += 1;
         }
-        const uint32_t lo = n ? (v[0] | (v[1] << 16)) : 0u;
-        const uint32_t hi = n ? ((v[2] << 16) | (n << 10) | (((32u - first_len) & 31u) << 5) |
-                                 ((32u - pos) & 31u))
-                              : 0u;
-        emit[2 * p] = lo;
-        emit[2 * p + 1] = hi;
+        if (n) {
+            slot[0] |= (32u - pos) & 31u;
+            slot[1] |= n;
+        }
+        emit[2 * p] = slot[0] | (slot[1] << 16);
+        emit[2 * p + 1] = slot[2] | (slot[3] << 16);
     }
     return DF11_OK;
 }

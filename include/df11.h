@@ -139,8 +139,8 @@ df11_status df11_validate(const df11_sections *s);
 /* Decode tables for the GPU kernel, derived from the 256 code lengths: a
  * hierarchy of 256-entry tables indexed by 8 stream bits each (the pages'
  * compact LUTs, section "Decodage fonde sur des LUT hierarchiques"), with
- * 32-bit entries, followed by a 2048-entry count table and a 1024-entry emit
- * table that resolve several codes per lookup (16 KiB).  df11_tables_size
+ * 32-bit entries, followed by a 1024-entry count table and a 2048-entry emit
+ * table that resolve several codes per lookup (20 KiB).  df11_tables_size
  * reports the bytes needed and the number of hierarchical tables;
  * df11_build_tables writes them to dst (host memory, dst_bytes at least that
  * size).  Errors: DF11_E_INVALID_ARG, DF11_E_FORMAT (lengths do
@@ -185,10 +185,10 @@ df11_status df11_decode_block(const df11_device_block *blk, uint16_t *out_bf16,
 /* Kernel variants (the output never depends on the choice):
  *  DF11_VARIANT_SINGLE: one code per table lookup in both phases, 8-bit
  *    indexed hierarchical tables only (the pages' kernel design);
- *  DF11_VARIANT_MULTI: phase 1 takes every code that ends in the next 11 bits
- *    per lookup (count table), phase 2 up to three codes in the next 10 bits
- *    (emit table); codes longer than that and the last one or two codes of a
- *    window go through the hierarchical tables.  The default. */
+ *  DF11_VARIANT_MULTI: phase 1 takes every code that ends in the next 10 bits
+ *    per lookup (count table), phase 2 up to four codes in the next 11 bits
+ *    (emit table); longer codes go through the hierarchical tables.  The
+ *    default. */
 #define DF11_VARIANT_SINGLE 1u
 #define DF11_VARIANT_MULTI 2u
 

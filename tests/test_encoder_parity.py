@@ -98,7 +98,7 @@ def test_tables_decode_every_oracle_codeword(case):
     codes = oracle.canonical_codes(ln)
     t = hdb.df11_build_tables(ln.astype(np.uint8)).view(np.uint32)
     nb, nt = hdb.df11_tables_size(ln.astype(np.uint8))
-    assert nb == t.nbytes == nt * 1024 + 2048 * 4 + 1024 * 8
+    assert nb == t.nbytes == nt * 1024 + 1024 * 4 + 2048 * 8
     for e in np.nonzero(ln)[0]:
         bits = format(int(codes[e]), "0{}b".format(int(ln[e])))
         # any continuation bits must not change the result
@@ -179,10 +179,10 @@ def test_count_and_emit_tables(case):
     complete = len(by_bits) > 1
     t = hdb.df11_build_tables(ln.astype(np.uint8)).view(np.uint32)
     _, nt = hdb.df11_tables_size(ln.astype(np.uint8))
-    count = t[nt * 256: nt * 256 + 2048]
-    emit = t[nt * 256 + 2048:].reshape(1024, 2)
-    for p in range(2048):
-        got = _greedy(format(p, "011b"), by_bits, complete, 11)
+    count = t[nt * 256: nt * 256 + 1024]
+    emit = t[nt * 256 + 1024:].reshape(2048, 2)
+    for p in range(1024):
+        got = _greedy(format(p, "010b"), by_bits, complete, 10)
         tb = sum(L for _, L in got)
         mask = 0
         pos = 0
@@ -191,17 +191,19 @@ def test_count_and_emit_tables(case):
             pos += L
         want = (mask << 20) | tb if tb else 0
         assert int(count[p]) == want, (p, hex(int(count[p])), hex(want))
-    for p in range(1024):
-        got = _greedy(format(p, "010b"), by_bits, complete, 3)
+    for p in range(2048):
+        got = _greedy(format(p, "011b"), by_bits, complete, 4)
         lo, hi = int(emit[p, 0]), int(emit[p, 1])
-        n = (hi >> 10) & 3
-        assert n == len(got)
+        slots = [lo & 0xFFFF, lo >> 16, hi & 0xFFFF, hi >> 16]
         if not got:
             assert lo == 0 and hi == 0
             continue
-        vals = [e << 7 for e, _ in got] + [0, 0]
+        n = len(got)
         tb = sum(L for _, L in got)
-        assert lo == vals[0] | (vals[1] << 16)
-        assert hi >> 16 == vals[2]
-        assert hi & 31 == (32 - tb) & 31
-        assert (hi >> 5) & 31 == (32 - got[0][1]) & 31
+        assert slots[1] & 0x7F == n
+        assert slots[0] & 0x7F == (32 - tb) & 31
+        for k in range(4):
+            want = (got[k][0] << 7) if k < n else 0
+            assert slots[k] & 0x7F80 == want
+            if k >= 2:
+                assert slots[k] & 0x7F == 0
