@@ -186,7 +186,7 @@ template <bool kDeepGlobal>
 __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et, const KParams &p, uint32_t h,
                                            uint32_t l, uint32_t r, uint16_t *dst, uint32_t left) {
     typedef uint64_t u64_a2 __attribute__((aligned(2)));  // staging slots are 2-byte aligned
-    while (left > 0) {
+    while (left >= df11i::kEmitCodes) {
         const uint64_t ev = *reinterpret_cast<const uint64_t *>(et + (h >> (32 - df11i::kEmitBits)));
         const uint32_t lo = static_cast<uint32_t>(ev);
         const uint32_t n = (lo >> 16) & 7u;
@@ -195,14 +195,24 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
             --left;
             continue;
         }
-        if (left >= df11i::kEmitCodes) {
-            *reinterpret_cast<u64_a2 *>(dst) = ev;
-        } else {
-            dst[0] = static_cast<uint16_t>(lo);
-            if (left > 1) dst[1] = static_cast<uint16_t>(lo >> 16);
-            if (left > 2) dst[2] = static_cast<uint16_t>(ev >> 32);
-            if (n >= left) break;  // the last values of this window are written
+        *reinterpret_cast<u64_a2 *>(dst) = ev;
+        consume(lo, h, l, r);
+        dst += n;
+        left -= n;
+    }
+    while (left > 0) {  // the last one to three values: write only those
+        const uint64_t ev = *reinterpret_cast<const uint64_t *>(et + (h >> (32 - df11i::kEmitBits)));
+        const uint32_t lo = static_cast<uint32_t>(ev);
+        const uint32_t n = (lo >> 16) & 7u;
+        if (n == 0u) {
+            *dst++ = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
+            --left;
+            continue;
         }
+        dst[0] = static_cast<uint16_t>(lo);
+        if (left > 1) dst[1] = static_cast<uint16_t>(lo >> 16);
+        if (left > 2) dst[2] = static_cast<uint16_t>(ev >> 32);
+        if (n >= left) break;
         consume(lo, h, l, r);
         dst += n;
         left -= n;
@@ -215,36 +225,56 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
 __shared__ __align__(16) uint32_t s_count_table[df11i::kCountEntries];
 __shared__ __align__(16) uint2 s_emit_table[df11i::kEmitEntries];
 
-// Everything a unit needs from HBM before decoding: the lane's window words
-// (8 bytes + 4-byte halo), its two gap bytes (assembled only when used: any
-// computation on a load result makes the wave wait for it) and the unit's
-// output range.  Loaded one unit ahead so the latency overlaps the previous
-// unit.  u is uniform, so every address is a scalar base plus a lane offset.
-struct UnitInputs {
-    uint32_t w0, w1, w2, gap2;
-    uint64_t p0, p1;
-};
+// Buffer resources: a base address and a size in scalar registers, accessed
+// with 32-bit per-lane offsets.  Loads past the size return 0 and stores past
+// it are dropped, so masked accesses need an out-of-range offset rather than
+// a branch.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOff = 0x80000000u;  // an offset past every resource used here
+constexpr int kNonTemporal = 2;        // cache policy bit of buffer stores: non-temporal
 
-__device__ __forceinline__ void load_unit(const KParams &p, uint64_t u, uint32_t lane, UnitInputs &in) {
-    in.w0 = in.w1 = in.w2 = in.gap2 = 0;
-    const uint64_t w = u * 64 + lane;
-    if (w < p.n_windows) {
-        const uint8_t *sbase = p.stream + 512 * u;
-        const uint2 a = *reinterpret_cast<const uint2 *>(sbase + 8 * lane);
-        in.w0 = a.x;
-        in.w1 = a.y;
-        in.w2 = *reinterpret_cast<const uint32_t *>(sbase + 8 * lane + 8);
-        const uint8_t *gp = p.gaps + 40 * u + ((5 * lane) >> 3);
-        in.gap2 = gp[0] | (static_cast<uint32_t>(gp[1]) << 8);
-    }
-    in.p0 = p.unit_pos[u];
-    in.p1 = p.unit_pos[u + 1];
+__device__ __forceinline__ Rsrc rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
 }
 
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
     return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, uint32_t k) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), k);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), k);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Everything a unit needs from HBM before decoding: the lane's window words
+// (8 bytes + 4-byte halo), its two gap bytes (assembled only when used: any
+// computation on a load result makes the wave wait for it) and the unit's
+// output range.  Loaded one unit ahead so the latency overlaps the previous
+// unit.  Straight-line code: the compiler can then count the loads in flight
+// exactly and wait only for the ones it needs.
+struct UnitInputs {
+    uint32_t w0, w1, w2, g0, g1;
+    uint64_t pos;  // unit_pos[u] in even lanes, unit_pos[u + 1] in odd lanes
+};
+
+__device__ __forceinline__ void load_unit(const KParams &p, uint64_t u, uint32_t lane, UnitInputs &in) {
+    const Rsrc st = rsrc(p.stream + 512 * u, 528);  // the unit's 64 windows + 16-byte guard
+    const v2u a = __builtin_amdgcn_raw_buffer_load_b64(st, 8 * lane, 0, 0);
+    in.w0 = a.x;
+    in.w1 = a.y;
+    in.w2 = __builtin_amdgcn_raw_buffer_load_b32(st, 8 * lane + 8, 0, 0);
+    const Rsrc gp = rsrc(p.gaps + 40 * u, 48);
+    in.g0 = __builtin_amdgcn_raw_buffer_load_b8(gp, (5 * lane) >> 3, 0, 0);
+    in.g1 = __builtin_amdgcn_raw_buffer_load_b8(gp, ((5 * lane) >> 3) + 1, 0, 0);
+    const Rsrc up = rsrc(p.unit_pos + u, 16);
+    const v2u q = __builtin_amdgcn_raw_buffer_load_b64(up, 8 * (lane & 1), 0, 0);
+    in.pos = (static_cast<uint64_t>(q.y) << 32) | q.x;
 }
 
 constexpr int kPrefetchChunks = 4;  // 8-output chunks of sign/mantissa per lane loaded early
@@ -254,7 +284,7 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
                                             const uint2 *et, uint16_t *stage, uint32_t lane, uint64_t u,
                                             const UnitInputs &in, const UnitInputs &next) {
     // output range of the unit (uniform): staged element k is output base + k
-    const uint64_t q1 = uniform_u64(in.p1), q0 = uniform_u64(in.p0);
+    const uint64_t q1 = lane_u64(in.pos, 1), q0 = lane_u64(in.pos, 0);
     const uint64_t P1 = q1 < p.n_total ? q1 : p.n_total;
     const uint64_t P0 = q0 < P1 ? q0 : P1;
     const uint64_t base = P0 & ~uint64_t{7};
@@ -262,22 +292,22 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     const uint32_t span = span64 < p.stage_elems ? static_cast<uint32_t>(span64) : p.stage_elems;
     const uint32_t lead = static_cast<uint32_t>(P0 - base);  // staged slots before P0
     const uint32_t chunks = (span + 7) / 8;
-    const uint8_t *smb = p.sm + base;
-    uint16_t *outb = p.out + base;
+    const Rsrc smr = rsrc(p.sm + base, 8 * chunks);
 
     // sign/mantissa bytes of the unit, requested before decoding starts
+    // (chunks past the unit read as 0)
     uint2 smv[kPrefetchChunks];
 #pragma unroll
     for (int k = 0; k < kPrefetchChunks; ++k) {
-        const uint32_t c = lane + 64u * k;
-        smv[k] = c < chunks ? *reinterpret_cast<const uint2 *>(smb + 8u * c) : make_uint2(0, 0);
+        const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * (lane + 64u * k), 0, 0);
+        smv[k] = make_uint2(t.x, t.y);
     }
 
     // ---- this lane's window: gap and end (bits of the stream left in it)
     const uint64_t left = p.total_bits - 4096 * u;  // > 0 for every unit
     const uint32_t ulim = left < 4096 ? static_cast<uint32_t>(left) : 4096u;
     const int end = ulim > 64 * lane ? static_cast<int>(ulim - 64 * lane < 64 ? ulim - 64 * lane : 64) : 0;
-    const uint32_t gap2 = ((in.gap2 & 0xFFu) << 8) | (in.gap2 >> 8);  // big-endian 16 bits
+    const uint32_t gap2 = (in.g0 << 8) | in.g1;  // big-endian 16 bits
     const uint32_t gap = (gap2 >> (11u - ((5 * lane) & 7))) & 31u;
     const uint32_t w0 = __builtin_bswap32(in.w0), w1 = __builtin_bswap32(in.w1), w2 = __builtin_bswap32(in.w2);
 
@@ -308,47 +338,52 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     // ---- merge with sign/mantissa and store outputs [lead, span) of the
     // staging.  All of the unit's outputs are computed before its first
     // store: vmcnt is in order, so a wait for a load issued before a store
-    // would also wait for that store.
+    // would also wait for that store.  Chunks [full_lo, full_hi) lie inside
+    // the unit and go out as 16-byte stores; the at most two partial chunks
+    // (first and last) are written back merged to their staging slots and
+    // stored element by element by lanes 0..15.
     auto merge_chunk = [&](uint32_t c, uint2 sm) {
         const uint4 ev = *reinterpret_cast<const uint4 *>(stage + 8 * c);
-        uint4 o;
+        v4u o;
         o.x = merge2(ev.x, sm.x, 0x01010000u);
         o.y = merge2(ev.y, sm.x, 0x03030202u);
         o.z = merge2(ev.z, sm.y, 0x01010000u);
         o.w = merge2(ev.w, sm.y, 0x03030202u);
         return o;
     };
-    auto store_chunk = [&](uint32_t c, const uint4 &o) {
-        const uint32_t k0 = 8 * c;
-        if (k0 >= lead && k0 + 8 <= span) {
-            // the output is written once and not read back here: non-temporal
-            typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-            const v4u ov = {o.x, o.y, o.z, o.w};
-            __builtin_nontemporal_store(ov, reinterpret_cast<v4u *>(outb + k0));
-        } else {
-            const uint32_t v[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-            for (uint32_t k = 0; k < 8; ++k)
-                if (k0 + k >= lead && k0 + k < span) outb[k0 + k] = static_cast<uint16_t>(v[k >> 1] >> (16 * (k & 1)));
-        }
+    const uint32_t full_lo = lead ? 1u : 0u;
+    const uint32_t full_hi = span / 8;
+    const Rsrc outr = rsrc(p.out + base, 16 * full_hi);  // full chunks only
+    auto put_chunk = [&](uint32_t c, const v4u &o) {
+        // the output is written once and not read back here: non-temporal
+        __builtin_amdgcn_raw_buffer_store_b128(o, outr, c >= full_lo ? 16 * c : kOff, 0, kNonTemporal);
+        if ((c < full_lo || c >= full_hi) && c < chunks)
+            *reinterpret_cast<v4u *>(stage + 8 * c) = o;  // partial: finished below
     };
-    uint4 outv[kPrefetchChunks];
+    v4u outv[kPrefetchChunks];
 #pragma unroll
-    for (int k = 0; k < kPrefetchChunks; ++k) {
-        const uint32_t c = lane + 64u * k;
-        outv[k] = c < chunks ? merge_chunk(c, smv[k]) : make_uint4(0, 0, 0, 0);
-    }
+    for (int k = 0; k < kPrefetchChunks; ++k) outv[k] = merge_chunk(lane + 64u * k, smv[k]);
     // The next unit's inputs were requested before this unit's sign/mantissa
     // loads, so they have arrived; taking them here keeps the copy into the
     // current set (after the stores) from waiting on the stores.
-    asm volatile("" ::"v"(next.w0), "v"(next.w1), "v"(next.w2), "v"(next.gap2), "v"(next.p0), "v"(next.p1));
+    asm volatile("" ::"v"(next.w0), "v"(next.w1), "v"(next.w2), "v"(next.g0), "v"(next.g1), "v"(next.pos));
 #pragma unroll
-    for (int k = 0; k < kPrefetchChunks; ++k) {
-        const uint32_t c = lane + 64u * k;
-        if (c < chunks) store_chunk(c, outv[k]);
+    for (int k = 0; k < kPrefetchChunks; ++k) put_chunk(lane + 64u * k, outv[k]);
+    for (uint32_t c = lane + 64u * kPrefetchChunks; c < chunks; c += 64) {  // units above 2,048 outputs
+        const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * c, 0, 0);
+        put_chunk(c, merge_chunk(c, make_uint2(t.x, t.y)));
     }
-    for (uint32_t c = lane + 64u * kPrefetchChunks; c < chunks; c += 64)  // units above 2,048 outputs
-        store_chunk(c, merge_chunk(c, *reinterpret_cast<const uint2 *>(smb + 8u * c)));
+    wave_sync();
+    {
+        // lanes 0..7: chunk 0; lanes 8..15: the last chunk (if not chunk 0);
+        // every other lane (or element outside the unit) stores out of range
+        const uint32_t ec = lane < 8 ? 0u : chunks - 1;
+        const uint32_t k = 8 * ec + (lane & 7);
+        const bool mine = lane < 16 && chunks > 0 && (ec < full_lo || ec >= full_hi) && (lane < 8 || ec > 0) &&
+                          k >= lead && k < span;
+        const uint16_t v = stage[mine ? k : 0];
+        __builtin_amdgcn_raw_buffer_store_b16(v, rsrc(p.out + base, 2 * span), mine ? 2 * k : kOff, 0, 0);
+    }
     wave_sync();
 }
 
@@ -386,17 +421,23 @@ df11_decode_kernel(KParams p) {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
     uint16_t *stage = reinterpret_cast<uint16_t *>(lds + lds_tables * 1024u) + wave * p.stage_elems;
-    const uint64_t stride = uint64_t{gridDim.x} * waves;
+    const uint64_t stride = uniform_u64(uint64_t{gridDim.x} * waves);
 
-    uint64_t u = uint64_t{blockIdx.x} * waves + wave;
+    uint64_t u = uniform_u64(uint64_t{blockIdx.x} * waves + wave);
+    if (u >= p.n_units) return;  // uniform across the wave
+    const uint64_t last = p.n_units - 1;
     UnitInputs cur;
-    if (u < p.n_units) load_unit(p, u, lane, cur);
-    while (u < p.n_units) {  // uniform across the wave
-        UnitInputs nxt = {0, 0, 0, 0, 0, 0};
-        if (u + stride < p.n_units) load_unit(p, u + stride, lane, nxt);
+    load_unit(p, u, lane, cur);
+    while (true) {
+        // the next unit's inputs (a repeat of the last unit at the end, so the
+        // loads are unconditional)
+        uint64_t un = uniform_u64(u + stride);
+        UnitInputs nxt;
+        load_unit(p, un < last ? un : last, lane, nxt);
         decode_unit<kDeepGlobal, kMulti>(p, lut, s_count_table, s_emit_table, stage, lane, u, cur, nxt);
+        if (un >= p.n_units) break;
         cur = nxt;  // waits for the next unit's inputs, requested a whole unit ago
-        u += stride;
+        u = un;
     }
 }
 
