@@ -42,6 +42,7 @@ struct KParams {
     const uint64_t *unit_pos;
     uint16_t *out;
     uint64_t n_total, total_bits, n_windows, n_units;
+    uint32_t last_unit_bits;  // stream bits in the last unit (1..4096)
     uint32_t n_tables;
     uint32_t stage_elems;  // 16-bit staging elements per wave, multiple of 8
 };
@@ -80,9 +81,11 @@ __device__ __forceinline__ uint32_t lookup(const uint32_t *lut, const uint32_t *
 // (0..31) into the window words w0:w1:w2.
 __device__ __forceinline__ void start_at(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t g, uint32_t &h,
                                          uint32_t &l, uint32_t &r) {
-    h = g ? __builtin_amdgcn_alignbit(w0, w1, 32u - g) : w0;
-    l = g ? __builtin_amdgcn_alignbit(w1, w2, 32u - g) : w1;
-    r = w2 << g;
+    const uint64_t a = ((static_cast<uint64_t>(w0) << 32) | w1) << g;
+    const uint64_t b = ((static_cast<uint64_t>(w1) << 32) | w2) << g;
+    h = static_cast<uint32_t>(a >> 32);
+    l = static_cast<uint32_t>(b >> 32);
+    r = static_cast<uint32_t>(b);
 }
 
 // Consume one code: a leaf entry's low 5 bits hold (32 - length) & 31, which
@@ -141,32 +144,49 @@ __device__ __forceinline__ uint32_t count_single(const uint32_t *lut, const KPar
     return cnt;
 }
 
-// Phase 1 with the count table: every lookup takes all the codes that end
-// inside the next 11 bits; only those starting before the window end (rem
-// bits from here) are counted.  `S` holds the window from the current code
+// Phase 1 with the count table: `S` holds the window from the current code
 // start, followed by zeros instead of the 4-byte halo: only the last code
 // that starts inside the window can reach past it, and as the code is prefix
 // free, its zero-padded decode is longer than the window bits it covers, so
 // the next start it implies lies past the end and is not counted.
+//
+// While more than 10 window bits remain, every code of an entry starts
+// inside the window and the entry's count is taken whole (two steps per loop
+// test while more than 20 remain); the last steps count only the starts
+// before the end, from the entry's start mask.  An escape entry (first code
+// longer than the index) shifts by 0 and subtracts 128 from `rem`, which ends
+// both loops without a test in the loop body; the code is then taken from
+// the hierarchical tables and the loops resume.
 template <bool kDeepGlobal>
 __device__ __forceinline__ uint32_t count_multi(const uint32_t *lut, const uint32_t *ct, const KParams &p,
                                                 uint64_t S, int rem) {
     uint32_t cnt = 0;
-    while (rem > 0) {
-        const uint32_t top = static_cast<uint32_t>(S >> 32);
-        const uint32_t e = ct[top >> (32 - df11i::kCountBits)];
-        if (__builtin_expect(e == 0u, 0)) {  // first code longer than the index
-            const int len = entry_length(lookup<kDeepGlobal>(lut, p.tables, p.n_tables, top));
-            S <<= len;
-            rem -= len;
-            ++cnt;
-            continue;
-        }
-        const uint32_t w = rem < static_cast<int>(df11i::kCountBits) ? static_cast<uint32_t>(rem)
-                                                                    : df11i::kCountBits;
-        cnt += __popc(__builtin_amdgcn_ubfe(e, 20u, w));
+    auto full = [&]() {
+        const uint32_t e = ct[static_cast<uint32_t>(S >> (64 - df11i::kCountBits))];
+        cnt += (e >> 8) & 0xFFu;
         S <<= (e & 63u);
-        rem -= static_cast<int>(e & 63u);
+        rem -= static_cast<int>(e & 0xFFu);
+    };
+    while (true) {
+        while (rem > 2 * static_cast<int>(df11i::kCountBits)) {
+            full();
+            full();
+        }
+        if (rem > static_cast<int>(df11i::kCountBits)) full();
+        while (rem > 0) {
+            const uint32_t e = ct[static_cast<uint32_t>(S >> (64 - df11i::kCountBits))];
+            cnt += __popc(__builtin_amdgcn_ubfe(e, 20u, static_cast<uint32_t>(rem)));
+            S <<= (e & 63u);
+            rem -= static_cast<int>(e & 0xFFu);
+        }
+        // rem is now in (-10, 0] when done, or lowered by 128 per escape
+        const int fix = (64 - rem) & ~127;
+        if (__builtin_expect(fix == 0, 1)) break;
+        rem += fix;
+        const int len = entry_length(lookup<kDeepGlobal>(lut, p.tables, p.n_tables, static_cast<uint32_t>(S >> 32)));
+        S <<= len;
+        rem -= len;
+        ++cnt;
     }
     return cnt;
 }
@@ -178,44 +198,70 @@ __device__ __forceinline__ void emit_single(const uint32_t *lut, const KParams &
     for (uint32_t j = 0; j < n; ++j) dst[j] = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
 }
 
-// Phase 2 with the emit table: up to four codes per lookup.  While at least
-// four values remain, the whole 8-byte entry is stored (slots past the codes
-// actually taken belong to this lane and are overwritten next); in the last
-// step only the remaining slots are written.
-template <bool kDeepGlobal>
-__device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et, const KParams &p, uint32_t h,
-                                           uint32_t l, uint32_t r, uint16_t *dst, uint32_t left) {
-    typedef uint64_t u64_a2 __attribute__((aligned(2)));  // staging slots are 2-byte aligned
-    while (left >= df11i::kEmitCodes) {
-        const uint64_t ev = *reinterpret_cast<const uint64_t *>(et + (h >> (32 - df11i::kEmitBits)));
-        const uint32_t lo = static_cast<uint32_t>(ev);
-        const uint32_t n = (lo >> 16) & 7u;
-        if (__builtin_expect(n == 0u, 0)) {  // first code longer than the index
-            *dst++ = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
-            --left;
-            continue;
-        }
-        *reinterpret_cast<u64_a2 *>(dst) = ev;
-        consume(lo, h, l, r);
-        dst += n;
-        left -= n;
+// Phase 2 with the emit table keeps the 96-bit look-ahead h:l:r as two
+// 64-bit pairs, A = h:l and B = l:r: shifting both left by t and copying
+// B's high half into A's low half advances by t bits for any t in 0..32, so
+// an entry's t (its low bits) is applied as it is, and t = 0 is a no-op.
+struct Look96 {
+    uint64_t A, B;
+    __device__ __forceinline__ uint32_t h() const { return static_cast<uint32_t>(A >> 32); }
+    __device__ __forceinline__ void shift(uint32_t t) {
+        A <<= (t & 63u);
+        B <<= (t & 63u);
+        A = (A & 0xFFFFFFFF00000000ull) | (B >> 32);
     }
-    while (left > 0) {  // the last one to three values: write only those
-        const uint64_t ev = *reinterpret_cast<const uint64_t *>(et + (h >> (32 - df11i::kEmitBits)));
+};
+
+// Up to four codes per lookup.  While at least four values remain, the whole
+// 8-byte entry is stored (slots past the codes actually taken belong to this
+// lane and are overwritten next).  An escape entry (first code longer than
+// the index) shifts by 0 and takes 64 from `left`, which ends the loop with
+// no test in its body; the lane then undoes that, takes the code from the
+// hierarchical tables and goes back in.  The last one to three values are
+// written slot by slot: slots 1 and 2 go to their place or, when not taken,
+// onto slot 0's, and slot 0 is written last (LDS writes of one lane land in
+// program order).
+template <bool kDeepGlobal>
+__device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et, const KParams &p, Look96 s,
+                                           uint16_t *dst, int left) {
+    typedef uint64_t u64_a2 __attribute__((aligned(2)));  // staging slots are 2-byte aligned
+    auto entry = [&]() { return *reinterpret_cast<const uint64_t *>(et + (s.h() >> (32 - df11i::kEmitBits))); };
+    auto escape_step = [&]() {
+        const uint32_t e = lookup<kDeepGlobal>(lut, p.tables, p.n_tables, s.h());
+        *dst++ = static_cast<uint16_t>(e >> 16);
+        s.shift(static_cast<uint32_t>(entry_length(e)));
+        --left;
+    };
+    while (true) {
+        while (left >= static_cast<int>(df11i::kEmitCodes)) {
+            const uint64_t ev = entry();
+            const uint32_t lo = static_cast<uint32_t>(ev);
+            const uint32_t m = (lo >> 16) & 127u;  // n, or 64 for an escape
+            *reinterpret_cast<u64_a2 *>(dst) = ev;
+            s.shift(lo);
+            dst += m;
+            left -= static_cast<int>(m);
+        }
+        if (__builtin_expect(left >= 0, 1)) break;
+        left += static_cast<int>(df11i::kEmitEscape);
+        dst -= df11i::kEmitEscape;
+        escape_step();
+    }
+    while (left > 0) {
+        const uint64_t ev = entry();
         const uint32_t lo = static_cast<uint32_t>(ev);
-        const uint32_t n = (lo >> 16) & 7u;
-        if (n == 0u) {
-            *dst++ = static_cast<uint16_t>(single_step<kDeepGlobal>(lut, p, h, l, r) >> 16);
-            --left;
+        const uint32_t m = (lo >> 16) & 127u;
+        if (__builtin_expect(m == df11i::kEmitEscape, 0)) {
+            escape_step();
             continue;
         }
+        const int k = static_cast<int>(m) < left ? static_cast<int>(m) : left;
+        dst[k >= 2 ? 1 : 0] = static_cast<uint16_t>(lo >> 16);
+        dst[k >= 3 ? 2 : 0] = static_cast<uint16_t>(ev >> 32);
         dst[0] = static_cast<uint16_t>(lo);
-        if (left > 1) dst[1] = static_cast<uint16_t>(lo >> 16);
-        if (left > 2) dst[2] = static_cast<uint16_t>(ev >> 32);
-        if (n >= left) break;
-        consume(lo, h, l, r);
-        dst += n;
-        left -= n;
+        s.shift(lo);  // past the lane's last code the state is not used
+        dst += k;
+        left -= k;
     }
 }
 
@@ -277,7 +323,8 @@ __device__ __forceinline__ void load_unit(const KParams &p, uint64_t u, uint32_t
     in.pos = (static_cast<uint64_t>(q.y) << 32) | q.x;
 }
 
-constexpr int kPrefetchChunks = 4;  // 8-output chunks of sign/mantissa per lane loaded early
+constexpr uint32_t kChunksPerPass = 64;  // 8-output chunks, one per lane
+constexpr int kPrefetchChunks = 4;        // passes whose sign/mantissa bytes are loaded early
 
 template <bool kDeepGlobal, bool kMulti>
 __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lut, const uint32_t *ct,
@@ -294,19 +341,35 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     const uint32_t chunks = (span + 7) / 8;
     const Rsrc smr = rsrc(p.sm + base, 8 * chunks);
 
+    // Chunks [full_lo, full_hi) lie inside the unit and go out as 16-byte
+    // stores; the at most two partial chunks (the first when the unit starts
+    // inside it, the last when the unit ends inside it) go out element by
+    // element from lanes 0..7 (first chunk) and 8..15 (last chunk).
+    const uint32_t full_lo = lead ? 1u : 0u;
+    const uint32_t full_hi = span / 8;
+    const uint32_t ec = lane < 8 ? 0u : chunks - 1;
+    const uint32_t ek = 8 * ec + (lane & 7);
+    const bool edge = lane < 16 && chunks > 0 && (ec < full_lo || ec >= full_hi) && (lane < 8 || ec > 0) &&
+                      ek >= lead && ek < span;
+
     // sign/mantissa bytes of the unit, requested before decoding starts
     // (chunks past the unit read as 0)
     uint2 smv[kPrefetchChunks];
+    const bool pass3 = chunks > 3 * kChunksPerPass;  // uniform
 #pragma unroll
     for (int k = 0; k < kPrefetchChunks; ++k) {
-        const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * (lane + 64u * k), 0, 0);
+        if (k == 3 && !pass3) {
+            smv[k] = make_uint2(0u, 0u);
+            continue;
+        }
+        const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * (lane + kChunksPerPass * k), 0, 0);
         smv[k] = make_uint2(t.x, t.y);
     }
+    const uint32_t esm = __builtin_amdgcn_raw_buffer_load_b8(smr, edge ? ek : kOff, 0, 0);
 
     // ---- this lane's window: gap and end (bits of the stream left in it)
-    const uint64_t left = p.total_bits - 4096 * u;  // > 0 for every unit
-    const uint32_t ulim = left < 4096 ? static_cast<uint32_t>(left) : 4096u;
-    const int end = ulim > 64 * lane ? static_cast<int>(ulim - 64 * lane < 64 ? ulim - 64 * lane : 64) : 0;
+    const uint32_t ulim = u == p.n_units - 1 ? p.last_unit_bits : 4096u;
+    const int end = min(max(static_cast<int>(ulim) - 64 * static_cast<int>(lane), 0), 64);
     const uint32_t gap2 = (in.g0 << 8) | in.g1;  // big-endian 16 bits
     const uint32_t gap = (gap2 >> (11u - ((5 * lane) & 7))) & 31u;
     const uint32_t w0 = __builtin_bswap32(in.w0), w1 = __builtin_bswap32(in.w1), w2 = __builtin_bswap32(in.w2);
@@ -314,11 +377,16 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     // ---- phase 1: count the codes that start in [gap, end)
     uint32_t cnt;
     uint32_t h, l, r;
-    start_at(w0, w1, w2, gap, h, l, r);
+    Look96 look;
     if constexpr (kMulti) {
-        const uint64_t S = ((static_cast<uint64_t>(w0) << 32) | w1) << gap;
-        cnt = count_multi<kDeepGlobal>(lut, ct, p, S, end - static_cast<int>(gap));
+        // A = h:l and B = l:r, the window words from the gap on (A's low half
+        // is B's high half: it carries the halo bits that enter l)
+        look.B = ((static_cast<uint64_t>(w1) << 32) | w2) << gap;
+        const uint64_t a = ((static_cast<uint64_t>(w0) << 32) | w1) << gap;
+        look.A = (a & 0xFFFFFFFF00000000ull) | (look.B >> 32);
+        cnt = count_multi<kDeepGlobal>(lut, ct, p, look.A, end - static_cast<int>(gap));
     } else {
+        start_at(w0, w1, w2, gap, h, l, r);
         cnt = count_single<kDeepGlobal>(lut, p, h, l, r, static_cast<int>(gap), end);
     }
 
@@ -330,18 +398,14 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     const uint32_t room = first < p.stage_elems ? p.stage_elems - first : 0u;
     const uint32_t n2 = cnt < room ? cnt : room;  // never past this wave's staging
     if constexpr (kMulti)
-        emit_multi<kDeepGlobal>(lut, et, p, h, l, r, stage + first, n2);
+        emit_multi<kDeepGlobal>(lut, et, p, look, stage + first, static_cast<int>(n2));
     else
         emit_single<kDeepGlobal>(lut, p, h, l, r, stage + first, n2);
     wave_sync();
 
-    // ---- merge with sign/mantissa and store outputs [lead, span) of the
-    // staging.  All of the unit's outputs are computed before its first
-    // store: vmcnt is in order, so a wait for a load issued before a store
-    // would also wait for that store.  Chunks [full_lo, full_hi) lie inside
-    // the unit and go out as 16-byte stores; the at most two partial chunks
-    // (first and last) are written back merged to their staging slots and
-    // stored element by element by lanes 0..15.
+    // ---- merge with sign/mantissa and store.  All of the unit's outputs are
+    // computed before its first store: vmcnt is in order, so a wait for a load
+    // issued before a store would also wait for that store.
     auto merge_chunk = [&](uint32_t c, uint2 sm) {
         const uint4 ev = *reinterpret_cast<const uint4 *>(stage + 8 * c);
         v4u o;
@@ -351,40 +415,35 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
         o.w = merge2(ev.w, sm.y, 0x03030202u);
         return o;
     };
-    const uint32_t full_lo = lead ? 1u : 0u;
-    const uint32_t full_hi = span / 8;
     const Rsrc outr = rsrc(p.out + base, 16 * full_hi);  // full chunks only
+    // the output is written once and not read back here: non-temporal
     auto put_chunk = [&](uint32_t c, const v4u &o) {
-        // the output is written once and not read back here: non-temporal
         __builtin_amdgcn_raw_buffer_store_b128(o, outr, c >= full_lo ? 16 * c : kOff, 0, kNonTemporal);
-        if ((c < full_lo || c >= full_hi) && c < chunks)
-            *reinterpret_cast<v4u *>(stage + 8 * c) = o;  // partial: finished below
     };
     v4u outv[kPrefetchChunks];
 #pragma unroll
-    for (int k = 0; k < kPrefetchChunks; ++k) outv[k] = merge_chunk(lane + 64u * k, smv[k]);
+    for (int k = 0; k < 3; ++k) outv[k] = merge_chunk(lane + kChunksPerPass * k, smv[k]);
+    if (pass3) outv[3] = merge_chunk(lane + kChunksPerPass * 3, smv[3]);
+    // the edge element: bit 15 = sign, bits 6..0 = mantissa from its sm byte
+    const uint32_t st = stage[edge ? ek : 0];
+    const uint32_t eo = __builtin_amdgcn_perm(esm, esm, 0x0c0c0000u);  // sm byte in both bytes
+    const uint32_t eout = (eo & 0x807Fu) | (st & 0x7F80u);
     // The next unit's inputs were requested before this unit's sign/mantissa
     // loads, so they have arrived; taking them here keeps the copy into the
     // current set (after the stores) from waiting on the stores.
     asm volatile("" ::"v"(next.w0), "v"(next.w1), "v"(next.w2), "v"(next.g0), "v"(next.g1), "v"(next.pos));
 #pragma unroll
-    for (int k = 0; k < kPrefetchChunks; ++k) put_chunk(lane + 64u * k, outv[k]);
-    for (uint32_t c = lane + 64u * kPrefetchChunks; c < chunks; c += 64) {  // units above 2,048 outputs
-        const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * c, 0, 0);
-        put_chunk(c, merge_chunk(c, make_uint2(t.x, t.y)));
+    for (int k = 0; k < 3; ++k) put_chunk(lane + kChunksPerPass * k, outv[k]);
+    if (pass3) put_chunk(lane + kChunksPerPass * 3, outv[3]);
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(eout), rsrc(p.out + base, 2 * span),
+                                          edge ? 2 * ek : kOff, 0, 0);
+    if (chunks > kChunksPerPass * kPrefetchChunks) {  // units above 2,048 outputs (uniform)
+        for (uint32_t c = lane + kChunksPerPass * kPrefetchChunks; c < chunks; c += kChunksPerPass) {
+            const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * c, 0, 0);
+            put_chunk(c, merge_chunk(c, make_uint2(t.x, t.y)));
+        }
     }
-    wave_sync();
-    {
-        // lanes 0..7: chunk 0; lanes 8..15: the last chunk (if not chunk 0);
-        // every other lane (or element outside the unit) stores out of range
-        const uint32_t ec = lane < 8 ? 0u : chunks - 1;
-        const uint32_t k = 8 * ec + (lane & 7);
-        const bool mine = lane < 16 && chunks > 0 && (ec < full_lo || ec >= full_hi) && (lane < 8 || ec > 0) &&
-                          k >= lead && k < span;
-        const uint16_t v = stage[mine ? k : 0];
-        __builtin_amdgcn_raw_buffer_store_b16(v, rsrc(p.out + base, 2 * span), mine ? 2 * k : kOff, 0, 0);
-    }
-    wave_sync();
+    wave_sync();  // the staging is rewritten by the next unit
 }
 
 // Register budget: 8 waves per SIMD (64 VGPRs), the most a CU can hold;
@@ -570,6 +629,7 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     p.total_bits = blk->total_bits;
     p.n_windows = blk->n_windows;
     p.n_units = blk->n_units;
+    p.last_unit_bits = static_cast<uint32_t>(blk->total_bits - 4096 * (blk->n_units - 1));
     p.n_tables = blk->n_tables;
     p.stage_elems = stage_elems;
 

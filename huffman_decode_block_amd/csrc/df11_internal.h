@@ -30,20 +30,26 @@ constexpr uint32_t kFillerEntry = leaf_entry(0, 1);
 // same canonical code):
 //   count table, indexed by the next kCountBits stream bits, 32-bit entries:
 //     bits 29..20 = start mask (bit 20+j set when a code starts at offset j and
-//     ends inside the index bits), bits 5..0 = bits taken by those complete
-//     codes (t, also the shift amount of a 64-bit shift), other bits 0; an
-//     entry of 0 means the first code is longer than kCountBits.
+//     ends inside the index bits), bits 15..8 = number of those codes, bits
+//     7..0 = t, the bits they take (also the amount of a 64-bit shift, which
+//     reads only bits 5..0).  When the first code is longer than kCountBits
+//     the entry is kCountEscape: no codes, t = 128 (a shift by 0, and a step
+//     large enough that a decoder's remaining-bits count turns negative).
 //   emit table, indexed by the next kEmitBits bits, 64-bit entries holding
 //     four 16-bit slots, slot k = (exponent_k << 7) | field_k, for the first
 //     n = min(4, complete codes) codes.  An exponent shifted into its BF16
-//     position leaves bits 6..0 free, which carry: field_0 = (32 - t) & 31
-//     with t the bits of the n codes (the alignbit amount), field_1 = n.
-//     n = 0 means the first code is longer than kEmitBits.  Slots past n are
-//     0.  The whole entry can be written to a staging buffer as is: a reader
-//     takes only bits 14..7 of a slot.
+//     position leaves bits 6..0 free, which carry: field_0 = t, the bits of
+//     the n codes (also the amount of a 64-bit shift, which reads only bits
+//     5..0 of the entry), field_1 = n.  When the first code is longer than
+//     kEmitBits the entry has t = 0 and field_1 = kEmitEscape (64), a step
+//     that shifts by nothing and is too long for any lane's remaining count.
+//     Slots past n are 0.  The whole entry can be written to a staging
+//     buffer as is: a reader takes only bits 14..7 of a slot.
 constexpr uint32_t kCountBits = 10;
+constexpr uint32_t kCountEscape = 128;
 constexpr uint32_t kEmitBits = 11;
 constexpr uint32_t kEmitCodes = 4;
+constexpr uint32_t kEmitEscape = 64;
 constexpr uint32_t kCountEntries = 1u << kCountBits;
 constexpr uint32_t kEmitEntries = 1u << kEmitBits;
 constexpr uint64_t kMultiTableBytes = uint64_t{kCountEntries} * 4 + uint64_t{kEmitEntries} * 8;

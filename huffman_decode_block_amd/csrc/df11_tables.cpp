@@ -105,15 +105,16 @@ df11_status build_tables(const uint8_t code_len[256], uint32_t *dst, uint64_t ds
     // count table: every code that starts and ends inside the index bits
     uint32_t *count = dst + t.size();
     for (uint32_t p = 0; p < kCountEntries; ++p) {
-        uint32_t pos = 0, mask = 0;
+        uint32_t pos = 0, mask = 0, n = 0;
         while (pos < kCountBits) {
             const uint32_t window = (p << (32 - kCountBits)) << pos;
             const uint32_t l = entry_length(walk(t, window));
             if (l > kCountBits - pos) break;
             mask |= 1u << pos;
             pos += l;
+            n += 1;
         }
-        count[p] = pos ? (mask << 20) | pos : 0u;
+        count[p] = pos ? (mask << 20) | (n << 8) | pos : kCountEscape;
     }
     // emit table: up to four codes that end inside the index bits
     uint32_t *emit = count + kCountEntries;
@@ -129,8 +130,10 @@ df11_status build_tables(const uint8_t code_len[256], uint32_t *dst, uint64_t ds
             n += 1;
         }
         if (n) {
-            slot[0] |= (32u - pos) & 31u;
+            slot[0] |= pos;
             slot[1] |= n;
+        } else {
+            slot[1] = kEmitEscape;
         }
         emit[2 * p] = slot[0] | (slot[1] << 16);
         emit[2 * p + 1] = slot[2] | (slot[3] << 16);

@@ -189,19 +189,19 @@ def test_count_and_emit_tables(case):
         for _, L in got:
             mask |= 1 << pos
             pos += L
-        want = (mask << 20) | tb if tb else 0
+        want = (mask << 20) | (len(got) << 8) | tb if tb else 128  # 128: first code longer than 10 bits
         assert int(count[p]) == want, (p, hex(int(count[p])), hex(want))
     for p in range(2048):
         got = _greedy(format(p, "011b"), by_bits, complete, 4)
         lo, hi = int(emit[p, 0]), int(emit[p, 1])
         slots = [lo & 0xFFFF, lo >> 16, hi & 0xFFFF, hi >> 16]
-        if not got:
-            assert lo == 0 and hi == 0
+        if not got:  # first code longer than 11 bits: t = 0, field_1 = 64
+            assert lo == 64 << 16 and hi == 0
             continue
         n = len(got)
         tb = sum(L for _, L in got)
         assert slots[1] & 0x7F == n
-        assert slots[0] & 0x7F == (32 - tb) & 31
+        assert slots[0] & 0x7F == tb
         for k in range(4):
             want = (got[k][0] << 7) if k < n else 0
             assert slots[k] & 0x7F80 == want
