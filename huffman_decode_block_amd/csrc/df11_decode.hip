@@ -212,39 +212,63 @@ struct Look96 {
     }
 };
 
-// Up to four codes per lookup.  While at least four values remain, the whole
-// 8-byte entry is stored (slots past the codes actually taken belong to this
-// lane and are overwritten next).  An escape entry (first code longer than
-// the index) shifts by 0 and takes 64 from `left`, which ends the loop with
-// no test in its body; the lane then undoes that, takes the code from the
-// hierarchical tables and goes back in.  The last one to three values are
-// written slot by slot: slots 1 and 2 go to their place or, when not taken,
-// onto slot 0's, and slot 0 is written last (LDS writes of one lane land in
-// program order).
+// Up to four codes per lookup.  The staging is zeroed before phase 2 and
+// every entry is ORed, shifted to the lane's next slot, into the two aligned
+// 8-byte words it covers: aligned LDS accesses are far cheaper than 2-byte
+// aligned ones, and OR needs no order between lanes.  Slots of an entry past
+// its n codes have zero exponent bits, and the control fields sit below the
+// exponent, so the extra bits an entry ORs in never reach an exponent.  An
+// escape entry (first code longer than the index) shifts by 0, ORs nothing
+// but control bits and takes 64 from `left`, which ends the loop with no test
+// in its body; the lane then undoes that, takes the code from the
+// hierarchical tables and goes back in.  Only the lane's last entry may hold
+// codes past its range; it is masked to the codes the lane owns.
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
+
+struct StageCursor {
+    lds_u64 *w;   // aligned word holding the next slot
+    uint32_t fb;  // bit offset of that slot in the word: 0, 16, 32, 48
+    __device__ __forceinline__ void put(uint64_t ev, uint32_t n) {
+        __hip_atomic_fetch_or(w, ev << fb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+        // the slots that do not fit: ev >> (64 - fb), and nothing when fb = 0
+        __hip_atomic_fetch_or(w + 1, (ev >> (48u - fb)) >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+        fb += n << 4;
+        w += fb >> 6;
+        fb &= 63u;
+    }
+};
+
 template <bool kDeepGlobal>
 __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et, const KParams &p, Look96 s,
-                                           uint16_t *dst, int left) {
-    typedef uint64_t u64_a2 __attribute__((aligned(2)));  // staging slots are 2-byte aligned
+                                           uint16_t *stage, uint32_t first, int left) {
+    StageCursor cur;
+    // the staging is LDS: the low 32 bits of its generic address are the LDS address
+    cur.w = reinterpret_cast<lds_u64 *>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage)) + 2u * (first & ~3u));
+    cur.fb = (first & 3u) << 4;
     auto entry = [&]() { return *reinterpret_cast<const uint64_t *>(et + (s.h() >> (32 - df11i::kEmitBits))); };
     auto escape_step = [&]() {
         const uint32_t e = lookup<kDeepGlobal>(lut, p.tables, p.n_tables, s.h());
-        *dst++ = static_cast<uint16_t>(e >> 16);
+        cur.put(e >> 16, 1u);  // a leaf entry's bits 30..16 are exponent << 7
         s.shift(static_cast<uint32_t>(entry_length(e)));
         --left;
     };
     while (true) {
+        // Each step's ORs are issued after the next step's table read: LDS
+        // operations complete in order, so a wait for the read then leaves
+        // the ORs in flight.
+        uint64_t ev = entry();
+        asm volatile("" ::"v"(ev));  // wait here, not at the loop head
         while (left >= static_cast<int>(df11i::kEmitCodes)) {
-            const uint64_t ev = entry();
             const uint32_t lo = static_cast<uint32_t>(ev);
             const uint32_t m = (lo >> 16) & 127u;  // n, or 64 for an escape
-            *reinterpret_cast<u64_a2 *>(dst) = ev;
             s.shift(lo);
-            dst += m;
+            const uint64_t ev_next = entry();  // past the last step: read, not used
+            cur.put(ev, m & 7u);
             left -= static_cast<int>(m);
+            ev = ev_next;
         }
         if (__builtin_expect(left >= 0, 1)) break;
         left += static_cast<int>(df11i::kEmitEscape);
-        dst -= df11i::kEmitEscape;
         escape_step();
     }
     while (left > 0) {
@@ -255,13 +279,10 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
             escape_step();
             continue;
         }
-        const int k = static_cast<int>(m) < left ? static_cast<int>(m) : left;
-        dst[k >= 2 ? 1 : 0] = static_cast<uint16_t>(lo >> 16);
-        dst[k >= 3 ? 2 : 0] = static_cast<uint16_t>(ev >> 32);
-        dst[0] = static_cast<uint16_t>(lo);
+        const uint32_t k = m < static_cast<uint32_t>(left) ? m : static_cast<uint32_t>(left);
+        cur.put(ev & ((uint64_t{1} << (16 * k)) - 1), k);  // k < 4 here
         s.shift(lo);  // past the lane's last code the state is not used
-        dst += k;
-        left -= k;
+        left -= static_cast<int>(k);
     }
 }
 
@@ -367,6 +388,11 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     }
     const uint32_t esm = __builtin_amdgcn_raw_buffer_load_b8(smr, edge ? ek : kOff, 0, 0);
 
+    if constexpr (kMulti) {  // phase 2 ORs into the staging
+        for (uint32_t i = lane; i < p.stage_elems / 8u; i += kChunksPerPass)
+            reinterpret_cast<uint4 *>(stage)[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
     // ---- this lane's window: gap and end (bits of the stream left in it)
     const uint32_t ulim = u == p.n_units - 1 ? p.last_unit_bits : 4096u;
     const int end = min(max(static_cast<int>(ulim) - 64 * static_cast<int>(lane), 0), 64);
@@ -395,10 +421,13 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
 
     // ---- phase 2: decode again, stage (exponent << 7) at the output slot
     const uint32_t first = lead + excl;
-    const uint32_t room = first < p.stage_elems ? p.stage_elems - first : 0u;
-    const uint32_t n2 = cnt < room ? cnt : room;  // never past this wave's staging
+    // never past this wave's staging (the multi-code path writes whole
+    // 8-byte words, up to 8 slots past its last one)
+    const uint32_t limit = kMulti ? p.stage_elems - 8u : p.stage_elems;
+    const uint32_t room = first < limit ? limit - first : 0u;
+    const uint32_t n2 = cnt < room ? cnt : room;
     if constexpr (kMulti)
-        emit_multi<kDeepGlobal>(lut, et, p, look, stage + first, static_cast<int>(n2));
+        emit_multi<kDeepGlobal>(lut, et, p, look, stage, first, static_cast<int>(n2));
     else
         emit_single<kDeepGlobal>(lut, p, h, l, r, stage + first, n2);
     wave_sync();
@@ -431,7 +460,8 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     // The next unit's inputs were requested before this unit's sign/mantissa
     // loads, so they have arrived; taking them here keeps the copy into the
     // current set (after the stores) from waiting on the stores.
-    asm volatile("" ::"v"(next.w0), "v"(next.w1), "v"(next.w2), "v"(next.g0), "v"(next.g1), "v"(next.pos));
+    asm volatile("" ::"v"(next.w0), "v"(next.w1), "v"(next.w2), "v"(next.g0), "v"(next.g1), "v"(next.pos),
+                 "v"(eout));
 #pragma unroll
     for (int k = 0; k < 3; ++k) put_chunk(lane + kChunksPerPass * k, outv[k]);
     if (pass3) put_chunk(lane + kChunksPerPass * 3, outv[3]);
@@ -487,6 +517,11 @@ df11_decode_kernel(KParams p) {
     const uint64_t last = p.n_units - 1;
     UnitInputs cur;
     load_unit(p, u, lane, cur);
+    // Wait for the first unit's inputs here: the loop head then sees them
+    // complete on both of its entries, and needs no wait that would also
+    // drain the previous unit's stores (vmcnt counts loads and stores in
+    // issue order).
+    asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1), "v"(cur.pos));
     while (true) {
         // the next unit's inputs (a repeat of the last unit at the end, so the
         // loads are unconditional)
@@ -603,7 +638,10 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     // + one staging area per wave; it bounds how many waves are resident.
     const uint32_t lds_tables = deep_global ? 1u : blk->n_tables;
     const uint32_t fixed_static = multi ? static_cast<uint32_t>(df11i::kMultiTableBytes) : 0u;
-    const uint32_t stage_elems = static_cast<uint32_t>((blk->max_unit_count + 7 + 7) / 8 * 8);
+    // staging: the unit's outputs after up to 7 slots of lead, rounded to
+    // 8-output chunks, plus one 8-byte word that the multi-code path may OR
+    // past its last slot
+    const uint32_t stage_elems = static_cast<uint32_t>((blk->max_unit_count + 7 + 7) / 8 * 8 + 8);
     auto lds_for = [&](uint32_t w) { return lds_tables * 1024u + w * stage_elems * 2u; };
     uint32_t waves = 0, per_cu = 0;
     for (uint32_t w = 16; w >= 1; w >>= 1) {  // the geometry with the most resident waves
