@@ -219,59 +219,60 @@ struct Look96 {
 // its n codes have zero exponent bits, and the control fields sit below the
 // exponent, so the extra bits an entry ORs in never reach an exponent.  An
 // escape entry (first code longer than the index) shifts by 0, ORs nothing
-// but control bits and takes 64 from `left`, which ends the loop with no test
-// in its body; the lane then undoes that, takes the code from the
-// hierarchical tables and goes back in.  Only the lane's last entry may hold
-// codes past its range; it is masked to the codes the lane owns.
+// but control bits and moves the lane's cursor 64 slots on, which ends the
+// loop with no test in its body; the lane then undoes that, takes the code
+// from the hierarchical tables and goes back in.  Only the lane's last entry
+// may hold codes past its range; it is masked to the codes the lane owns.
 typedef __attribute__((address_space(3))) uint64_t lds_u64;
 
-struct StageCursor {
-    lds_u64 *w;   // aligned word holding the next slot
-    uint32_t fb;  // bit offset of that slot in the word: 0, 16, 32, 48
-    __device__ __forceinline__ void put(uint64_t ev, uint32_t n) {
-        __hip_atomic_fetch_or(w, ev << fb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-        // the slots that do not fit: ev >> (64 - fb), and nothing when fb = 0
-        __hip_atomic_fetch_or(w + 1, (ev >> (48u - fb)) >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-        fb += n << 4;
-        w += fb >> 6;
-        fb &= 63u;
-    }
-};
+// OR an entry into the staging at LDS byte address b (the lane's next slot):
+// the low part into the aligned word holding b, the slots that do not fit
+// into the next word.  Shift amounts are taken from b << 3, whose low 6 bits
+// (all that a 64-bit shift reads) are 16 x (slot index mod 4).
+__device__ __forceinline__ void stage_or(uint32_t b, uint64_t ev) {
+    lds_u64 *w = reinterpret_cast<lds_u64 *>(b & ~7u);
+    const uint32_t s8 = b << 3;
+    __hip_atomic_fetch_or(w, ev << (s8 & 63u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+    // ev >> (64 - shift), and nothing for a shift of 0
+    __hip_atomic_fetch_or(w + 1, (ev >> ((48u - s8) & 63u)) >> 16, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
 
 template <bool kDeepGlobal>
 __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et, const KParams &p, Look96 s,
-                                           uint16_t *stage, uint32_t first, int left) {
-    StageCursor cur;
+                                           uint16_t *stage, uint32_t first, uint32_t n) {
     // the staging is LDS: the low 32 bits of its generic address are the LDS address
-    cur.w = reinterpret_cast<lds_u64 *>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage)) + 2u * (first & ~3u));
-    cur.fb = (first & 3u) << 4;
+    uint32_t b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage)) + 2u * first;
+    const uint32_t bend = b + 2u * n;  // past the lane's last slot
+    const uint32_t bfull = bend - 2u * df11i::kEmitCodes;  // last start with four own slots (LDS addresses are far above 8)
     auto entry = [&]() { return *reinterpret_cast<const uint64_t *>(et + (s.h() >> (32 - df11i::kEmitBits))); };
     auto escape_step = [&]() {
         const uint32_t e = lookup<kDeepGlobal>(lut, p.tables, p.n_tables, s.h());
-        cur.put(e >> 16, 1u);  // a leaf entry's bits 30..16 are exponent << 7
+        stage_or(b, e >> 16);  // a leaf entry's bits 30..16 are exponent << 7
+        b += 2u;
         s.shift(static_cast<uint32_t>(entry_length(e)));
-        --left;
     };
     while (true) {
         // Each step's ORs are issued after the next step's table read: LDS
         // operations complete in order, so a wait for the read then leaves
-        // the ORs in flight.
+        // the ORs in flight.  An escape advances b by 64 slots, past bend
+        // (a lane has at most 53 codes left when it meets a code longer
+        // than the index), which ends the loop; it is then undone.
         uint64_t ev = entry();
         asm volatile("" ::"v"(ev));  // wait here, not at the loop head
-        while (left >= static_cast<int>(df11i::kEmitCodes)) {
+        while (b <= bfull) {
             const uint32_t lo = static_cast<uint32_t>(ev);
-            const uint32_t m = (lo >> 16) & 127u;  // n, or 64 for an escape
             s.shift(lo);
             const uint64_t ev_next = entry();  // past the last step: read, not used
-            cur.put(ev, m & 7u);
-            left -= static_cast<int>(m);
+            stage_or(b, ev);
+            b = __builtin_amdgcn_ubfe(lo, 16u, 7u) * 2u + b;  // n slots, or 64 for an escape
             ev = ev_next;
         }
-        if (__builtin_expect(left >= 0, 1)) break;
-        left += static_cast<int>(df11i::kEmitEscape);
+        if (__builtin_expect(b <= bend, 1)) break;
+        b -= 2u * df11i::kEmitEscape;
         escape_step();
     }
-    while (left > 0) {
+    while (b < bend) {  // the last one to three codes
         const uint64_t ev = entry();
         const uint32_t lo = static_cast<uint32_t>(ev);
         const uint32_t m = (lo >> 16) & 127u;
@@ -279,10 +280,11 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
             escape_step();
             continue;
         }
-        const uint32_t k = m < static_cast<uint32_t>(left) ? m : static_cast<uint32_t>(left);
-        cur.put(ev & ((uint64_t{1} << (16 * k)) - 1), k);  // k < 4 here
+        const uint32_t left = (bend - b) >> 1;
+        const uint32_t k = m < left ? m : left;
+        stage_or(b, ev & ((uint64_t{1} << (16 * k)) - 1));  // only the lane's own codes
+        b += 2u * k;
         s.shift(lo);  // past the lane's last code the state is not used
-        left -= static_cast<int>(k);
     }
 }
 
@@ -427,7 +429,7 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     const uint32_t room = first < limit ? limit - first : 0u;
     const uint32_t n2 = cnt < room ? cnt : room;
     if constexpr (kMulti)
-        emit_multi<kDeepGlobal>(lut, et, p, look, stage, first, static_cast<int>(n2));
+        emit_multi<kDeepGlobal>(lut, et, p, look, stage, first, n2);
     else
         emit_single<kDeepGlobal>(lut, p, h, l, r, stage + first, n2);
     wave_sync();
