@@ -84,12 +84,99 @@ def cpu_baseline(sections, x, min_seconds: float) -> dict:
                       f"tree walk, units split over {threads} threads; {el:.1f} s; output == input: {ok}"}
 
 
+def overlap_bench(args, dev) -> None:
+    """Exposed decode time per block when block i+1 is decoded on a side stream
+    while block i's seven GEMMs (torch F.linear, BF16, synthetic activations of
+    `batch` tokens) run: the pages' decompress-just-before-use schedule."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    import df11_inputs as di
+    import huffman_decode_block_amd as hdb
+    from huffman_decode_block_amd.overlap import DecodeAhead
+
+    wl = di.WORKLOADS[args.workload]
+    x = di.generate(args.workload)
+    enc = hdb.df11_encode_block(di.split(args.workload, x))
+    blk = hdb.DeviceBlock.from_encoded(enc, device=dev)
+    shapes = [(m.rows, m.cols) for m in wl.mats]
+    nb = args.overlap_blocks
+    ahead = DecodeAhead([blk] * nb, [shapes] * nb, device=dev)  # the same block nb times
+    ref = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    ref_views = hdb.matrix_views(ref, blk, shapes)
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn, reps=3):
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+
+    for bs in [int(v) for v in args.overlap.split(",") if v]:
+        g = torch.Generator(device=dev).manual_seed(bs)
+        acts = {c: torch.randn(bs, c, device=dev, generator=g).to(torch.bfloat16)
+                for c in sorted({c for _, c in shapes})}
+
+        def consume(i, views):
+            for v in views:
+                F.linear(acts[v.shape[1]], v)
+
+        def gemms_only():
+            for i in range(nb):
+                consume(i, ref_views)
+
+        def decodes_only():
+            for _ in range(nb):
+                hdb.df11_decode_block(blk, out=ahead.bufs[0][: blk.n_total], stream=stream)
+
+        for f in (gemms_only, decodes_only):  # warm up (clocks, GEMM algorithm choice)
+            for _ in range(3):
+                f()
+        torch.cuda.synchronize()
+        t_g, t_d = timed(gemms_only) / nb, timed(decodes_only) / nb
+        # The ahead-decode's footprint: the whole GPU, or a capped number of
+        # workgroups (it then streams on fewer CUs and leaves the rest to the
+        # GEMMs, which matters once they are compute-bound).
+        per_launch = {}
+        for wv, mg in ((0, 0), (0, 256), (8, 0), (8, 512), (4, 0), (4, 1024), (4, 512), (2, 0)):
+            ahead.launch = None if (wv, mg) == (0, 0) else (wv, mg, 0, 0)
+            for _ in range(2):
+                ahead.run(consume, stream=stream)
+            per_launch[(wv, mg)] = timed(lambda: ahead.run(consume, stream=stream)) / nb
+        ahead.launch = None
+        best = min(per_launch, key=per_launch.get)
+        t_p = per_launch[best]
+        name = lambda k: f"{k[0] or 'default'} waves/group, " + (f"{k[1]} groups" if k[1] else "default grid")  # noqa: E731
+        res = {
+            "metric": "exposed decode time per block, next block decoded on a side stream during this block's GEMMs",
+            "value": round((t_p - t_g) * 1e6, 2), "unit": "us", "higher_is_better": False,
+            "batch_tokens": bs, "blocks": nb, "workload": f"{args.workload}: {wl.description}",
+            "gemms_only_us_per_block": round(t_g * 1e6, 2),
+            "decode_only_us_per_block": round(t_d * 1e6, 2),
+            "pipelined_us_per_block": round(t_p * 1e6, 2),
+            "pipelined_over_bf16": round(t_p / t_g, 3),
+            "decode_launch": name(best),
+            "pipelined_us_by_decode_launch": {name(k): round(v * 1e6, 2) for k, v in per_launch.items()},
+        }
+        print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3", "C4", "C5"])
+    ap.add_argument("--workload", default="C3", choices=["C1", "C2", "C3", "C4", "C5", "E8"],
+                    help="C3 is the headline workload; E8 is a single embedding/LM-head-shaped matrix")
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0 = library default)")
     ap.add_argument("--max-groups", type=int, default=0)
     ap.add_argument("--oversubscribe", type=int, default=0,
@@ -101,6 +188,10 @@ def main():
                          "over the first ~10 ms of load after host-side work)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap", default="",
+                    help="comma-separated batch sizes: instead of the main line, measure the decode of block i+1 "
+                         "on a side stream overlapped with block i's GEMMs (one JSON line per batch)")
+    ap.add_argument("--overlap-blocks", type=int, default=12)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -127,6 +218,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
+
+    if args.overlap:
+        overlap_bench(args, dev)
         return
 
     wl = di.WORKLOADS[args.workload]

@@ -14,6 +14,9 @@ Workloads (stand-ins for real checkpoint weights, which are not available):
   C4  Llama-3.1-70B-shaped block (8192, 1024, 28672), sigma 0.015     seed 4
   C5  Llama-3.1-405B-shaped block (16384, 1024, 53248),
       0.01 * Student-t(df=3), i.i.d.                                  seed 5
+  E8  one Llama-3.1-8B token-embedding / LM-head-shaped matrix,
+      128256 x 4096, row r ~ N(0, (0.015 u_r)^2), u_r ~ U(0.5, 2),
+      its own codebook                                                seed 6
 
 Recipe (fixed, independent of the thread count): every matrix is cut into
 row blocks of ``ROW_BLOCK`` rows; block b of matrix m draws from
@@ -85,6 +88,9 @@ WORKLOADS = {
                    _llama_block(8192, 1024, 28672), "normal", 0.015, True, 4),
     "C5": Workload("C5", "Llama-3.1-405B-shaped transformer block, 0.01 x Student-t(3)",
                    _llama_block(16384, 1024, 53248), "t3", 0.01, False, 5),
+    "E8": Workload("E8", "Llama-3.1-8B token-embedding / LM-head-shaped matrix 128256x4096, "
+                   "N(0, 0.015) x U(0.5,2) row scale, own codebook",
+                   (Matrix("embed_tokens", 128256, 4096),), "normal", 0.015, True, 6, False),
 }
 
 
@@ -116,7 +122,7 @@ def _block_values(wl: Workload, m_idx: int, mat: Matrix, b: int) -> np.ndarray:
 
 
 def generate(key: str, threads: int | None = None) -> np.ndarray:
-    """Flat uint16 BF16 bits of workload `key` (C1..C5)."""
+    """Flat uint16 BF16 bits of workload `key` (C1..C5, E8)."""
     wl = WORKLOADS[key]
     out = np.empty(wl.numel, dtype=np.uint16)
     jobs = []

@@ -221,3 +221,9 @@ def test_workload_c4_full(torch):
 
 def test_workload_c5_full(torch):
     _full_block(torch, "C5", VARIANTS)
+
+
+def test_workload_e8_full(torch):
+    """A single large matrix with its own codebook: the token embedding / LM
+    head of a Llama-3.1-8B-shaped model (128256 x 4096), one launch."""
+    _full_block(torch, "E8", VARIANTS)
