@@ -34,14 +34,15 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic_bytes(s) -> dict:
+def algorithmic_bytes(s, with_counts: bool = False) -> dict:
     """Bytes one decode must move: the compressed payload read once plus the
     BF16 output written once (padding excluded)."""
     rd = ((s.total_bits + 7) // 8          # encoded exponents
           + s.n_total                      # sign/mantissa bytes
           + (5 * s.n_windows + 7) // 8     # 5-bit gaps
           + 8 * (s.n_units + 1)            # unit positions
-          + s.raw.tables_bytes)            # decode tables
+          + s.raw.tables_bytes             # decode tables
+          + (s.n_windows if with_counts else 0))  # per-window counts (counting-free variant)
     wr = 2 * s.n_total
     return {"read": int(rd), "write": int(wr), "total": int(rd + wr)}
 
@@ -182,7 +183,8 @@ def main():
     ap.add_argument("--oversubscribe", type=int, default=0,
                     help="workgroups per resident workgroup slot (0 = library default)")
     ap.add_argument("--variant", type=int, default=0,
-                    help="1 = one code per lookup, 2 = multi-code lookups (0 = library default)")
+                    help="1 = one code per lookup, 2 = multi-code lookups (0 = library default), "
+                         "3 = multi-code with stored per-window counts (a format variant)")
     ap.add_argument("--prewarm-ms", type=float, default=500.0,
                     help="untimed decodes before the warmup steps, for this long (the GPU's clocks ramp up "
                          "over the first ~10 ms of load after host-side work)")
@@ -226,7 +228,8 @@ def main():
 
     wl = di.WORKLOADS[args.workload]
     x = di.generate(args.workload)
-    enc = hdb.df11_encode_block(di.split(args.workload, x))
+    with_counts = args.variant == hdb.DF11_VARIANT_COUNTS
+    enc = hdb.df11_encode_block(di.split(args.workload, x), window_counts=with_counts)
     s = enc.sections
     blk = hdb.DeviceBlock.from_encoded(enc, device=dev)
     out = torch.empty(s.n_total, dtype=torch.bfloat16, device=dev)
@@ -280,7 +283,7 @@ def main():
     del xd
 
     n = int(s.n_total)
-    ab = algorithmic_bytes(s)
+    ab = algorithmic_bytes(s, with_counts)
     achieved = ab["total"] / k_avg / 1e9
     value = 2.0 * n * args.steps / wall / 1e9
     # the committed counters were taken on the default (multi-code) kernel
@@ -313,7 +316,8 @@ def main():
             "launch": {"waves_per_group": args.waves or "default", "max_groups": args.max_groups or "auto",
                        "oversubscribe": args.oversubscribe or "default",
                        "variant": {0: "default (multi-code)", 1: "one code per lookup",
-                                   2: "multi-code"}[args.variant]},
+                                   2: "multi-code",
+                                   3: "multi-code with stored per-window counts (format variant)"}[args.variant]},
         },
         "gweights_per_s": round(n * args.steps / wall / 1e9, 2),
         "pct_hbm_roofline": round(100.0 * ab["total"] * args.steps / wall / 1e9 / PEAK_HBM_GBS, 2),

@@ -54,6 +54,7 @@ class df11_sections(ctypes.Structure):
         ("off_code_len", _u64), ("off_mat_offset", _u64), ("off_stream", _u64),
         ("off_sign_mant", _u64), ("off_gaps", _u64), ("off_unit_pos", _u64), ("off_tables", _u64),
         ("exp_entropy_bits", ctypes.c_double), ("mean_code_len_bits", ctypes.c_double),
+        ("counts", _vp), ("counts_bytes", _u64), ("off_counts", _u64),
     ]
 
 
@@ -67,6 +68,7 @@ class df11_device_block(ctypes.Structure):
         ("n_total", _u64), ("total_bits", _u64), ("n_windows", _u64), ("n_units", _u64),
         ("max_unit_count", _u64),
         ("version", _u32), ("n_tables", _u32),
+        ("counts", _vp),
     ]
 
 
@@ -76,6 +78,8 @@ class df11_launch(ctypes.Structure):
 
 DF11_VARIANT_SINGLE = 1
 DF11_VARIANT_MULTI = 2
+DF11_VARIANT_COUNTS = 3
+DF11_ENCODE_WINDOW_COUNTS = 1
 
 
 class DF11Error(RuntimeError):
@@ -87,7 +91,7 @@ class DF11Error(RuntimeError):
 _lib = None
 
 EXPORTS = [
-    "df11_encode_block", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
+    "df11_encode_block", "df11_encode_block_ex", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
 ]
@@ -104,6 +108,8 @@ def lib():
     P = ctypes.POINTER
     L.df11_encode_block.argtypes = [P(df11_bf16_view), _u32, _u32, P(_vp)]
     L.df11_encode_block.restype = ctypes.c_int32
+    L.df11_encode_block_ex.argtypes = [P(df11_bf16_view), _u32, _u32, _u32, P(_vp)]
+    L.df11_encode_block_ex.restype = ctypes.c_int32
     L.df11_encoded_sections.argtypes = [_vp, P(df11_sections)]
     L.df11_encoded_sections.restype = ctypes.c_int32
     L.df11_encoded_free.argtypes = [_vp]
@@ -204,6 +210,8 @@ class Sections:
         self.unit_pos = _np_view(s.unit_pos, s.n_units + 1, np.uint64)
         self.tables = _np_view(s.tables, s.tables_bytes, np.uint8)
         self.blob = _np_view(s.blob, s.blob_bytes, np.uint8)
+        # optional per-window code counts (64 * n_units bytes), else None
+        self.counts = _np_view(s.counts, s.counts_bytes, np.uint8) if s.counts_bytes else None
 
     @property
     def compressed_bytes(self) -> int:
@@ -239,16 +247,26 @@ class Encoded:
         self.free()
 
 
-def df11_encode_block(mats, n_threads: int = 0) -> Encoded:
-    """Encode a list of BF16 matrices (host) as one block with one codebook."""
+def df11_encode_block(mats, n_threads: int = 0, window_counts: bool = False) -> Encoded:
+    """Encode a list of BF16 matrices (host) as one block with one codebook;
+    window_counts adds the per-window code counts (df11_encode_block_ex with
+    DF11_ENCODE_WINDOW_COUNTS)."""
     arrays = [_as_u16(m) for m in mats]
     views = (df11_bf16_view * max(1, len(arrays)))()
     for i, a in enumerate(arrays):
         views[i].data = a.ctypes.data if a.size else None
         views[i].numel = a.size
     h = _vp()
-    _check(lib().df11_encode_block(views, len(arrays), n_threads, ctypes.byref(h)), "df11_encode_block")
+    if window_counts:
+        _check(lib().df11_encode_block_ex(views, len(arrays), n_threads, DF11_ENCODE_WINDOW_COUNTS,
+                                          ctypes.byref(h)), "df11_encode_block_ex")
+    else:
+        _check(lib().df11_encode_block(views, len(arrays), n_threads, ctypes.byref(h)), "df11_encode_block")
     return Encoded(h.value)
+
+
+def df11_encode_block_ex(mats, n_threads: int = 0, flags: int = 0) -> Encoded:
+    return df11_encode_block(mats, n_threads, window_counts=bool(flags & DF11_ENCODE_WINDOW_COUNTS))
 
 
 def df11_encoded_sections(enc: Encoded) -> Sections:
@@ -307,16 +325,23 @@ class DeviceBlock:
 
     @classmethod
     def from_parts(cls, *, code_len, stream, sign_mant, gaps, unit_pos, n_total, total_bits,
-                   device="cuda") -> "DeviceBlock":
+                   counts=None, device="cuda") -> "DeviceBlock":
         """Device block from separately given host sections (for example the
-        oracle's); the decode tables are built here from code_len."""
+        oracle's); the decode tables are built here from code_len.  counts:
+        optional per-window code counts (padded here to 64 per unit)."""
         import torch
         tables = df11_build_tables(code_len)
         _, n_tables = df11_tables_size(code_len)
         up = np.ascontiguousarray(unit_pos, dtype=np.uint64)
         parts = {}
-        for name, arr in [("tables", tables), ("stream", stream), ("sign_mant", sign_mant),
-                          ("gaps", gaps), ("unit_pos", up.view(np.uint8))]:
+        arrays = [("tables", tables), ("stream", stream), ("sign_mant", sign_mant),
+                  ("gaps", gaps), ("unit_pos", up.view(np.uint8))]
+        if counts is not None:
+            nu = ((int(total_bits) + 63) // 64 + 63) // 64
+            c = np.zeros(64 * nu, dtype=np.uint8)
+            c[:len(counts)] = np.asarray(counts, dtype=np.uint8)[:64 * nu]
+            arrays.append(("counts", c))
+        for name, arr in arrays:
             a = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
             t = torch.empty(max(1, a.size), dtype=torch.uint8, device=device)
             if a.size:
@@ -336,6 +361,7 @@ class DeviceBlock:
         b.max_unit_count = int(d.max()) if d.size else 0
         b.version = DF11_FORMAT_VERSION
         b.n_tables = n_tables
+        b.counts = parts["counts"][0].data_ptr() if "counts" in parts else None
         return cls(b, [t for t, _ in parts.values()], n_total)
 
     def compressed_bytes(self) -> int:
@@ -394,7 +420,7 @@ def matrix_views(out, block_or_offsets, shapes=None):
 
 
 __all__ = [
-    "df11_encode_block", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
+    "df11_encode_block", "df11_encode_block_ex", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
     "Encoded", "Sections",

@@ -72,6 +72,19 @@ extern "C" df11_status df11_validate(const df11_sections *s) {
         if (start > s->total_bits) return DF11_E_FORMAT;
         if (start == s->total_bits && w + 1 != nw) return DF11_E_FORMAT;
     }
+    // optional per-window counts: at most 64 each, summing to each unit's count
+    if (s->counts_bytes) {
+        if (!s->counts || s->counts_bytes < 64 * nu) return DF11_E_FORMAT;
+        for (uint64_t u = 0; u < nu; ++u) {
+            uint64_t sum = 0;
+            for (uint64_t w = 64 * u; w < 64 * u + 64; ++w) {
+                const uint64_t c = s->counts[w];
+                if (c > 64 || (w >= nw && c != 0)) return DF11_E_FORMAT;
+                sum += c;
+            }
+            if (sum != s->unit_pos[u + 1] - s->unit_pos[u]) return DF11_E_FORMAT;
+        }
+    }
     return DF11_OK;
 }
 
@@ -96,6 +109,7 @@ extern "C" df11_status df11_device_block_from_blob(const df11_sections *s, const
     d.max_unit_count = s->max_unit_count;
     d.version = s->version;
     d.n_tables = s->n_tables;
+    d.counts = s->counts_bytes ? b + s->off_counts : nullptr;
     *out = d;
     return DF11_OK;
 }

@@ -40,6 +40,7 @@ struct KParams {
     const uint8_t *sm;
     const uint8_t *gaps;
     const uint64_t *unit_pos;
+    const uint8_t *counts;  // per-window code counts (the counting-free variant only)
     uint16_t *out;
     uint64_t n_total, total_bits, n_windows, n_units;
     uint32_t last_unit_bits;  // stream bits in the last unit (1..4096)
@@ -329,9 +330,11 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, uint32_t k) {
 // exactly and wait only for the ones it needs.
 struct UnitInputs {
     uint32_t w0, w1, w2, g0, g1;
+    uint32_t c;    // the window's stored code count (counting-free variant)
     uint64_t pos;  // unit_pos[u] in even lanes, unit_pos[u + 1] in odd lanes
 };
 
+template <bool kCounts>
 __device__ __forceinline__ void load_unit(const KParams &p, uint64_t u, uint32_t lane, UnitInputs &in) {
     const Rsrc st = rsrc(p.stream + 512 * u, 528);  // the unit's 64 windows + 16-byte guard
     const v2u a = __builtin_amdgcn_raw_buffer_load_b64(st, 8 * lane, 0, 0);
@@ -344,12 +347,13 @@ __device__ __forceinline__ void load_unit(const KParams &p, uint64_t u, uint32_t
     const Rsrc up = rsrc(p.unit_pos + u, 16);
     const v2u q = __builtin_amdgcn_raw_buffer_load_b64(up, 8 * (lane & 1), 0, 0);
     in.pos = (static_cast<uint64_t>(q.y) << 32) | q.x;
+    in.c = kCounts ? __builtin_amdgcn_raw_buffer_load_b8(rsrc(p.counts + 64 * u, 64), lane, 0, 0) : 0u;
 }
 
 constexpr uint32_t kChunksPerPass = 64;  // 8-output chunks, one per lane
 constexpr int kPrefetchChunks = 4;        // passes whose sign/mantissa bytes are loaded early
 
-template <bool kDeepGlobal, bool kMulti>
+template <bool kDeepGlobal, bool kMulti, bool kCounts>
 __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lut, const uint32_t *ct,
                                             const uint2 *et, uint16_t *stage, uint32_t lane, uint64_t u,
                                             const UnitInputs &in, const UnitInputs &next) {
@@ -412,7 +416,10 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
         look.B = ((static_cast<uint64_t>(w1) << 32) | w2) << gap;
         const uint64_t a = ((static_cast<uint64_t>(w0) << 32) | w1) << gap;
         look.A = (a & 0xFFFFFFFF00000000ull) | (look.B >> 32);
-        cnt = count_multi<kDeepGlobal>(lut, ct, p, look.A, end - static_cast<int>(gap));
+        if constexpr (kCounts)
+            cnt = in.c;  // stored with the block: the counting pass is skipped
+        else
+            cnt = count_multi<kDeepGlobal>(lut, ct, p, look.A, end - static_cast<int>(gap));
     } else {
         start_at(w0, w1, w2, gap, h, l, r);
         cnt = count_single<kDeepGlobal>(lut, p, h, l, r, static_cast<int>(gap), end);
@@ -463,7 +470,7 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     // loads, so they have arrived; taking them here keeps the copy into the
     // current set (after the stores) from waiting on the stores.
     asm volatile("" ::"v"(next.w0), "v"(next.w1), "v"(next.w2), "v"(next.g0), "v"(next.g1), "v"(next.pos),
-                 "v"(eout));
+                 "v"(next.c), "v"(eout));
 #pragma unroll
     for (int k = 0; k < 3; ++k) put_chunk(lane + kChunksPerPass * k, outv[k]);
     if (pass3) put_chunk(lane + kChunksPerPass * 3, outv[3]);
@@ -485,7 +492,7 @@ struct WavesPerEU {
     static constexpr int value = kDeepGlobal ? 4 : 8;
 };
 
-template <bool kDeepGlobal, bool kMulti>
+template <bool kDeepGlobal, bool kMulti, bool kCounts>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WavesPerEU<kDeepGlobal>::value)))
 df11_decode_kernel(KParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -506,6 +513,21 @@ df11_decode_kernel(KParams p) {
         }
     }
     __syncthreads();
+    if constexpr (kMulti) {
+        // Every count entry advances (1..10 bits) or is the escape, every emit
+        // entry takes 1..4 codes or is the escape: the loops over them then end
+        // whatever the stream holds.  Tables that break this store nothing.
+        bool bad = false;
+        for (uint32_t i = threadIdx.x; i < df11i::kCountEntries; i += blockDim.x) {
+            const uint32_t t = s_count_table[i] & 0xFFu;
+            bad |= !((t >= 1u && t <= df11i::kCountBits) || s_count_table[i] == df11i::kCountEscape);
+        }
+        for (uint32_t i = threadIdx.x; i < df11i::kEmitEntries; i += blockDim.x) {
+            const uint32_t m = (s_emit_table[i].x >> 16) & 127u;
+            bad |= !((m >= 1u && m <= df11i::kEmitCodes) || m == df11i::kEmitEscape);
+        }
+        if (__syncthreads_or(bad)) return;
+    }
 
     const uint32_t lane = threadIdx.x & 63u;
     // wave index and wave count are uniform: keep unit indices in scalar registers
@@ -518,19 +540,19 @@ df11_decode_kernel(KParams p) {
     if (u >= p.n_units) return;  // uniform across the wave
     const uint64_t last = p.n_units - 1;
     UnitInputs cur;
-    load_unit(p, u, lane, cur);
+    load_unit<kCounts>(p, u, lane, cur);
     // Wait for the first unit's inputs here: the loop head then sees them
     // complete on both of its entries, and needs no wait that would also
     // drain the previous unit's stores (vmcnt counts loads and stores in
     // issue order).
-    asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1), "v"(cur.pos));
+    asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1), "v"(cur.pos), "v"(cur.c));
     while (true) {
         // the next unit's inputs (a repeat of the last unit at the end, so the
         // loads are unconditional)
         uint64_t un = uniform_u64(u + stride);
         UnitInputs nxt;
-        load_unit(p, un < last ? un : last, lane, nxt);
-        decode_unit<kDeepGlobal, kMulti>(p, lut, s_count_table, s_emit_table, stage, lane, u, cur, nxt);
+        load_unit<kCounts>(p, un < last ? un : last, lane, nxt);
+        decode_unit<kDeepGlobal, kMulti, kCounts>(p, lut, s_count_table, s_emit_table, stage, lane, u, cur, nxt);
         if (un >= p.n_units) break;
         cur = nxt;  // waits for the next unit's inputs, requested a whole unit ago
         u = un;
@@ -614,8 +636,11 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     df11_status rc = check_block(blk, out_bf16, out_capacity);
     if (rc != DF11_OK || blk->n_total == 0) return rc;
     const uint32_t variant = (launch && launch->variant) ? launch->variant : DF11_VARIANT_MULTI;
-    if (variant != DF11_VARIANT_SINGLE && variant != DF11_VARIANT_MULTI) return DF11_E_INVALID_ARG;
-    const bool multi = variant == DF11_VARIANT_MULTI;
+    if (variant != DF11_VARIANT_SINGLE && variant != DF11_VARIANT_MULTI && variant != DF11_VARIANT_COUNTS)
+        return DF11_E_INVALID_ARG;
+    const bool counts = variant == DF11_VARIANT_COUNTS;
+    const bool multi = variant == DF11_VARIANT_MULTI || counts;
+    if (counts && !blk->counts) return DF11_E_INVALID_ARG;
     if (multi && blk->tables_bytes < df11i::tables_bytes_for(blk->n_tables)) return DF11_E_INVALID_ARG;
     const uint32_t asked = launch ? launch->waves_per_group : 0u;
     if (asked != 0 && asked != 1 && asked != 2 && asked != 4 && asked != 8 && asked != 16)
@@ -629,12 +654,15 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     const DeviceInfo info = device_info(dev);
     const bool deep_global = blk->n_tables > kLdsTableMax;
     const void *fn;
-    if (multi)
-        fn = deep_global ? reinterpret_cast<const void *>(&df11_decode_kernel<true, true>)
-                         : reinterpret_cast<const void *>(&df11_decode_kernel<false, true>);
+    if (counts)
+        fn = deep_global ? reinterpret_cast<const void *>(&df11_decode_kernel<true, true, true>)
+                         : reinterpret_cast<const void *>(&df11_decode_kernel<false, true, true>);
+    else if (multi)
+        fn = deep_global ? reinterpret_cast<const void *>(&df11_decode_kernel<true, true, false>)
+                         : reinterpret_cast<const void *>(&df11_decode_kernel<false, true, false>);
     else
-        fn = deep_global ? reinterpret_cast<const void *>(&df11_decode_kernel<true, false>)
-                         : reinterpret_cast<const void *>(&df11_decode_kernel<false, false>);
+        fn = deep_global ? reinterpret_cast<const void *>(&df11_decode_kernel<true, false, false>)
+                         : reinterpret_cast<const void *>(&df11_decode_kernel<false, false, false>);
 
     // LDS per workgroup: static (count and emit tables) + hierarchical tables
     // + one staging area per wave; it bounds how many waves are resident.
@@ -664,6 +692,7 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     p.sm = blk->sign_mant;
     p.gaps = blk->gaps;
     p.unit_pos = blk->unit_pos;
+    p.counts = blk->counts;
     p.out = out_bf16;
     p.n_total = blk->n_total;
     p.total_bits = blk->total_bits;

@@ -197,7 +197,13 @@ uint32_t thread_count(uint32_t requested) {
 
 extern "C" df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_mats,
                                          uint32_t n_threads, df11_encoded **out) {
-    if (!out || (n_mats && !mats)) return DF11_E_INVALID_ARG;
+    return df11_encode_block_ex(mats, n_mats, n_threads, 0u, out);
+}
+
+extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t n_mats,
+                                            uint32_t n_threads, uint32_t flags, df11_encoded **out) {
+    if (!out || (n_mats && !mats) || (flags & ~DF11_ENCODE_WINDOW_COUNTS)) return DF11_E_INVALID_ARG;
+    const bool with_counts = (flags & DF11_ENCODE_WINDOW_COUNTS) != 0;
     *out = nullptr;
     Source src{mats, std::vector<uint64_t>(n_mats + 1, 0)};
     for (uint32_t m = 0; m < n_mats; ++m) {
@@ -270,6 +276,8 @@ extern "C" df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_
     s.off_sign_mant = place(s.sign_mant_bytes);
     s.off_gaps = place(s.gaps_bytes);
     s.off_unit_pos = place(8 * (n_units + 1));
+    s.counts_bytes = with_counts ? 64 * n_units : 0;
+    s.off_counts = with_counts ? place(s.counts_bytes) : 0;
     s.blob_bytes = off;
 
     void *mem = nullptr;
@@ -294,6 +302,8 @@ extern "C" df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_
     uint64_t *words = reinterpret_cast<uint64_t *>(stream);  // stream as 64-bit words, bit 63 first
     const uint64_t n_words = s.stream_bytes / 8;
     std::vector<uint8_t> gap8(n_windows, 0xFF);
+    constexpr uint64_t kNoStart = ~uint64_t{0};
+    std::vector<uint64_t> wfirst(with_counts ? n_windows : 0, kNoStart);  // first element starting in w
 
     // zero the stream, the tails of the other sections; unit_pos starts at N
     run_parallel(T, [&](uint32_t t) {
@@ -340,7 +350,10 @@ extern "C" df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_
                 const uint32_t l = len32[e];
                 // first code start in its window / unit?
                 const uint64_t w = bit >> 6;
-                if (i == 0 || ((bit - prev_len) >> 6) < w) gap8[w] = static_cast<uint8_t>(bit - 64 * w);
+                if (i == 0 || ((bit - prev_len) >> 6) < w) {
+                    gap8[w] = static_cast<uint8_t>(bit - 64 * w);
+                    if (with_counts) wfirst[w] = i;
+                }
                 const uint64_t u = bit >> 12;
                 if (i == 0 || ((bit - prev_len) >> 12) < u) unit_pos[u] = i;
                 sm[i] = static_cast<uint8_t>(((x >> 8) & 0x80u) | (x & 0x7Fu));
@@ -393,6 +406,21 @@ extern "C" df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_
         }
     });
     unit_pos[n_units] = N;
+    if (with_counts) {  // codes starting in window w: up to the next window's first
+        uint8_t *counts = blob + s.off_counts;
+        std::memset(counts, 0, s.counts_bytes);
+        uint64_t next = N;
+        for (uint64_t w = n_windows; w-- > 0;) {
+            if (wfirst[w] == kNoStart) continue;  // only the last window may have none
+            const uint64_t c = next - wfirst[w];
+            if (c > 64) {
+                df11_encoded_free(enc);
+                return DF11_E_FORMAT;
+            }
+            counts[w] = static_cast<uint8_t>(c);
+            next = wfirst[w];
+        }
+    }
     uint64_t mu = 0;
     for (uint64_t u = 0; u < n_units; ++u) mu = std::max(mu, unit_pos[u + 1] - unit_pos[u]);
     enc->sec.max_unit_count = mu;
@@ -423,6 +451,7 @@ extern "C" df11_status df11_encoded_sections(const df11_encoded *enc, df11_secti
     out->gaps = b + out->off_gaps;
     out->unit_pos = reinterpret_cast<const uint64_t *>(b + out->off_unit_pos);
     out->tables = b + out->off_tables;
+    out->counts = out->counts_bytes ? b + out->off_counts : nullptr;
     return DF11_OK;
 }
 

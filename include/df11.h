@@ -112,6 +112,14 @@ typedef struct df11_sections {
         off_tables;
     double exp_entropy_bits;        /* Shannon entropy of the exponents, bits/weight */
     double mean_code_len_bits;      /* total_bits / n_total */
+    /* Optional per-window code counts (blobs encoded with
+     * DF11_ENCODE_WINDOW_COUNTS, else counts = NULL, counts_bytes = 0): byte w
+     * is the number of codes that start in window w, i.e. in bits
+     * [64w + gap_w, min(64w + 64, total_bits)); 0..64.  Padded with zeros to
+     * 64 * n_units bytes. */
+    const uint8_t *counts;
+    uint64_t counts_bytes;
+    uint64_t off_counts;
 } df11_sections;
 
 /* Encodes the concatenation of n_mats BF16 matrices with one shared codebook.
@@ -123,6 +131,18 @@ typedef struct df11_sections {
 df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_mats, uint32_t n_threads,
                               df11_encoded **out);
 
+/* Encoder options (bit flags). */
+#define DF11_ENCODE_WINDOW_COUNTS 1u  /* also store the per-window code counts */
+
+/* df11_encode_block with options.  DF11_ENCODE_WINDOW_COUNTS adds a section
+ * that is not part of the pages' format: the number of codes starting in
+ * each 64-bit window.  It costs one byte per window (about 1.3 % more bytes
+ * per decode at 2.7 bits per exponent) and lets DF11_VARIANT_COUNTS skip the
+ * counting pass.  Unknown flags: DF11_E_INVALID_ARG; otherwise as
+ * df11_encode_block. */
+df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t n_mats, uint32_t n_threads,
+                                 uint32_t flags, df11_encoded **out);
+
 /* Fills *out with views into enc.  Errors: DF11_E_INVALID_ARG. */
 df11_status df11_encoded_sections(const df11_encoded *enc, df11_sections *out);
 
@@ -132,8 +152,9 @@ void df11_encoded_free(df11_encoded *enc);
 /* Host-side structural check of the sections (sizes, code lengths form a
  * prefix code of at most 32 bits, gaps within [0, 31] and consistent with
  * total_bits, unit_pos non-decreasing from 0 to n_total, max_unit_count,
- * decode tables equal to the ones built from code_len).  It does not decode
- * the stream.  Returns DF11_OK or DF11_E_FORMAT / DF11_E_INVALID_ARG. */
+ * decode tables equal to the ones built from code_len, and when present, per
+ * window counts of at most 64 that sum over each unit to its unit_pos
+ * difference).  It does not decode the stream.  Returns DF11_OK or DF11_E_FORMAT / DF11_E_INVALID_ARG. */
 df11_status df11_validate(const df11_sections *s);
 
 /* Decode tables for the GPU kernel, derived from the 256 code lengths: a
@@ -164,6 +185,7 @@ typedef struct df11_device_block {
     uint64_t n_total, total_bits, n_windows, n_units, max_unit_count;
     uint32_t version;
     uint32_t n_tables;
+    const uint8_t *counts;          /* per-window counts, 64 * n_units bytes, or NULL */
 } df11_device_block;
 
 /* Fills *out for a device copy of a whole blob starting at device_blob. */
@@ -188,9 +210,16 @@ df11_status df11_decode_block(const df11_device_block *blk, uint16_t *out_bf16,
  *  DF11_VARIANT_MULTI: phase 1 takes every code that ends in the next 10 bits
  *    per lookup (count table), phase 2 up to four codes in the next 11 bits
  *    (emit table); longer codes go through the hierarchical tables.  The
- *    default. */
+ *    default.
+ *  DF11_VARIANT_COUNTS: DF11_VARIANT_MULTI with the counting pass replaced by
+ *    the stored per-window counts; needs blk->counts (a blob encoded with
+ *    DF11_ENCODE_WINDOW_COUNTS), else DF11_E_INVALID_ARG.  Not the pages'
+ *    format: a variant that trades one byte per window for the first pass.
+ * The multi-code kernels check the count and emit tables when they load them;
+ * with entries that no table builder writes, they store nothing. */
 #define DF11_VARIANT_SINGLE 1u
 #define DF11_VARIANT_MULTI 2u
+#define DF11_VARIANT_COUNTS 3u
 
 /* Launch geometry for df11_decode_block_ex (0 = automatic). */
 typedef struct df11_launch {

@@ -17,7 +17,8 @@ auxiliaires" (8-byte thread windows, 5-bit gaps, stored output positions).
 Parity status: every function here is pinned by the not-gpu tests (round
 trip on all BF16 patterns, Kraft equality, entropy bound, brute-force and
 dynamic-programming optimality, hand-derived vectors, vectorised
-re-derivation of gaps and positions).
+re-derivation of gaps and positions, a bit-by-bit walk of each window for the
+per-window counts).
 """
 from __future__ import annotations
 
@@ -216,6 +217,24 @@ def decode_units(enc: Encoded, u_begin: int = 0, u_end: int | None = None,
     if rc != 0:
         raise ValueError(f"orc_decode_units failed: {rc}")
     return out
+
+
+def window_counts(enc: Encoded, decoded=None) -> np.ndarray:
+    """Per-window code counts of a format variant that is not on the pages:
+    for each 64-bit window w, the number of codewords whose first bit lies in
+    [64w, 64w + 64).  As no codeword starts in [64w, 64w + gap_w) (definition
+    of the gap, hada.io summary, section "Noyau GPU en deux etapes et
+    metadonnees auxiliaires"), this is exactly the count of codes starting in
+    [64w + gap_w, min(64w + 64, total_bits)), the number that the decoder's
+    first phase computes for the window.  Code starts come from the oracle's
+    own decode of the stream (or `decoded`, its result, when already at hand):
+    start_i = sum of the code lengths of the exponents before i.  Returns
+    n_windows uint8 values (each at most 64)."""
+    x = decode(enc) if decoded is None else _u16(decoded)
+    lengths = enc.code_len.astype(np.int64)[(x >> 7) & 0xFF]
+    starts = np.concatenate([np.zeros(1, np.int64), np.cumsum(lengths)[:-1]]) if x.size else np.zeros(0, np.int64)
+    counts = np.bincount(starts >> 6, minlength=enc.n_windows)[:enc.n_windows]
+    return counts.astype(np.uint8)
 
 
 def exponent_entropy_bits(counts) -> float:

@@ -54,9 +54,10 @@ def check_oracle_sections(torch, x, name, variants=(0,)):
     o = oracle.encode(x)
     expect = oracle.decode(o)
     np.testing.assert_array_equal(expect, x)
+    counts = oracle.window_counts(o, decoded=expect) if hdb.DF11_VARIANT_COUNTS in variants else None
     blk = hdb.DeviceBlock.from_parts(code_len=o.code_len, stream=o.stream, sign_mant=o.sign_mant,
                                      gaps=o.gaps, unit_pos=o.unit_pos, n_total=o.n,
-                                     total_bits=o.total_bits)
+                                     total_bits=o.total_bits, counts=counts)
     for variant in variants:
         for poison in (0x5A5A, -1):
             say(f"{name}: oracle sections n={x.size} max_len={o.max_len} variant={variant} "
@@ -65,11 +66,12 @@ def check_oracle_sections(torch, x, name, variants=(0,)):
             np.testing.assert_array_equal(y, expect)
 
 
-VARIANTS = [hdb.DF11_VARIANT_SINGLE, hdb.DF11_VARIANT_MULTI]
+VARIANTS = [hdb.DF11_VARIANT_SINGLE, hdb.DF11_VARIANT_MULTI, hdb.DF11_VARIANT_COUNTS]
 
 
 def check_library_blob(torch, x, name, mats=None, launch=None):
-    enc = hdb.df11_encode_block(mats if mats is not None else [x])
+    with_counts = launch is not None and len(launch) > 2 and launch[2] == hdb.DF11_VARIANT_COUNTS
+    enc = hdb.df11_encode_block(mats if mats is not None else [x], window_counts=with_counts)
     s = enc.sections
     blk = hdb.DeviceBlock.from_encoded(enc)
     say(f"{name}: library blob n={x.size} tables={s.n_tables} max_len={s.max_code_len} launch={launch}")
@@ -167,6 +169,11 @@ def test_device_side_errors(torch):
     with pytest.raises(hdb.DF11Error) as ei:
         hdb.df11_decode_block(blk, out=big[1:])
     assert ei.value.status == hdb.DF11_E_INVALID_ARG
+    # the counting-free variant needs a blob with window counts
+    ok = torch.empty(x.size, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(hdb.DF11Error) as ei:
+        hdb.df11_decode_block(blk, out=ok, launch=(0, 0, hdb.DF11_VARIANT_COUNTS))
+    assert ei.value.status == hdb.DF11_E_INVALID_ARG
 
 
 def _full_block(torch, key, variants=(0,)):
@@ -174,7 +181,7 @@ def _full_block(torch, key, variants=(0,)):
     x = di.generate(key)
     mats = di.split(key, x)
     say(f"{key}: encoding {x.size} weights")
-    enc = hdb.df11_encode_block(mats)
+    enc = hdb.df11_encode_block(mats, window_counts=hdb.DF11_VARIANT_COUNTS in variants)
     s = enc.sections
     assert hdb.df11_validate(s) == hdb.DF11_OK
     blk = hdb.DeviceBlock.from_encoded(enc)
@@ -213,10 +220,11 @@ def test_workload_c3_full(torch):
     for a, b in [(s.stream, o.stream), (s.sign_mant, o.sign_mant), (s.gaps, o.gaps),
                  (s.unit_pos, o.unit_pos), (s.code_len, o.code_len)]:
         np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(s.counts[:s.n_windows], oracle.window_counts(o, decoded=x))
 
 
 def test_workload_c4_full(torch):
-    _full_block(torch, "C4")
+    _full_block(torch, "C4", (hdb.DF11_VARIANT_MULTI, hdb.DF11_VARIANT_COUNTS))
 
 
 def test_workload_c5_full(torch):
