@@ -303,7 +303,7 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr uint32_t kOff = 0x80000000u;  // an offset past every resource used here
-constexpr int kNonTemporal = 2;        // cache policy bit of buffer stores: non-temporal
+constexpr int kNonTemporal = 2;        // cache policy bit of buffer accesses: non-temporal
 
 __device__ __forceinline__ Rsrc rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
@@ -380,7 +380,7 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
                       ek >= lead && ek < span;
 
     // sign/mantissa bytes of the unit, requested before decoding starts
-    // (chunks past the unit read as 0)
+    // (chunks past the unit read as 0); read once, so non-temporal
     uint2 smv[kPrefetchChunks];
     const bool pass3 = chunks > 3 * kChunksPerPass;  // uniform
 #pragma unroll
@@ -389,7 +389,7 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
             smv[k] = make_uint2(0u, 0u);
             continue;
         }
-        const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * (lane + kChunksPerPass * k), 0, 0);
+        const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * (lane + kChunksPerPass * k), 0, kNonTemporal);
         smv[k] = make_uint2(t.x, t.y);
     }
     const uint32_t esm = __builtin_amdgcn_raw_buffer_load_b8(smr, edge ? ek : kOff, 0, 0);
@@ -478,7 +478,7 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
                                           edge ? 2 * ek : kOff, 0, 0);
     if (chunks > kChunksPerPass * kPrefetchChunks) {  // units above 2,048 outputs (uniform)
         for (uint32_t c = lane + kChunksPerPass * kPrefetchChunks; c < chunks; c += kChunksPerPass) {
-            const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * c, 0, 0);
+            const v2u t = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * c, 0, kNonTemporal);
             put_chunk(c, merge_chunk(c, make_uint2(t.x, t.y)));
         }
     }
