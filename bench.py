@@ -85,6 +85,90 @@ def cpu_baseline(sections, x, min_seconds: float) -> dict:
                       f"tree walk, units split over {threads} threads; {el:.1f} s; output == input: {ok}"}
 
 
+def gpu_encode_bench(args, dev) -> None:
+    """The GPU-side encoder on one block: histogram on the device, code lengths
+    on the host, offsets and packing on the device.  value = BF16 input bytes
+    encoded per second by the device passes (histogram + encode)."""
+    import numpy as np
+    import torch
+
+    import df11_inputs as di
+    import huffman_decode_block_amd as hdb
+
+    wl = di.WORKLOADS[args.workload]
+    x = di.generate(args.workload)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    g = hdb.gpu_encode(xd)  # allocates the sections once; checked below
+    s_host = hdb.df11_encode_block(di.split(args.workload, x)).sections
+    ok = (np.array_equal(g.section("stream")[:g.plan.stream_bytes], s_host.stream)
+          and np.array_equal(g.section("sign_mant")[:g.plan.sign_mant_bytes], s_host.sign_mant)
+          and np.array_equal(g.section("gaps")[:g.plan.gaps_bytes], s_host.gaps)
+          and np.array_equal(g.section("unit_pos").view(np.uint64), s_host.unit_pos))
+    if not ok:
+        raise SystemExit("GPU encoding differs from the host encoder; refusing to report a number")
+    t = g.tensors
+    hist = torch.empty(256, dtype=torch.int64, device=dev)
+
+    def encode_once():
+        hdb.df11_gpu_histogram(xd, hist, stream)
+        hdb.df11_gpu_encode(g.plan, xd, t["stream"], t["sign_mant"], t["gaps"], t["unit_pos"], None,
+                            t["workspace"], stream)
+
+    t_pre = time.perf_counter()
+    while (time.perf_counter() - t_pre) * 1e3 < args.prewarm_ms:
+        for _ in range(10):
+            encode_once()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        encode_once()
+    torch.cuda.synchronize()
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        encode_once()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = ev[0].elapsed_time(ev[1]) * 1e-3 / args.steps
+    n = int(x.size)
+    out_bytes = int(s_host.raw.stream_bytes + s_host.raw.sign_mant_bytes + s_host.raw.gaps_bytes
+                    + 8 * (s_host.n_units + 1))
+    algo = 2 * n + out_bytes  # the input read once, the sections written once
+    # CPU baselines: the library's host encoder (all cores of this process, at
+    # most 16) and the oracle's encoder (one thread); whole block, timed once
+    threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS") or 16))
+    c0 = time.perf_counter()
+    hdb.df11_encode_block(di.split(args.workload, x), n_threads=threads)
+    t_host = time.perf_counter() - c0
+    cpu = {"value": round(2.0 * n / t_host / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "host encoder",
+           "sample": f"whole block ({n} weights) encoded once by the library's host encoder, {threads} threads"}
+    if not args.no_cpu_baseline:
+        import oracle
+        c0 = time.perf_counter()
+        oracle.encode(x)
+        t_or = time.perf_counter() - c0
+        cpu_oracle = {"value": round(2.0 * n / t_or / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                      "sample": f"whole block ({n} weights) encoded once by the oracle (bit-serial, one thread)"}
+    else:
+        cpu_oracle = None
+    res = {
+        "metric": "GPU-side DF11 encode of one transformer block (BF16 input GB/s)",
+        "value": round(2.0 * n / per / 1e9, 2), "unit": "GB/s", "higher_is_better": True,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "data": "synthetic", "dtype": "u32",
+        "config": {"workload": f"{args.workload}: {wl.description}", "weights": n},
+        "encode_us": round(per * 1e6, 2),
+        "roofline": {"bound": "hbm", "achieved": round(algo / per / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(algo / per / 1e9 / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_step": algo,
+                     "note": "the device passes read the input three times (histogram, sums, pack)"},
+        "cpu_baseline": cpu,
+        "cpu_baseline_oracle": cpu_oracle,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def overlap_bench(args, dev) -> None:
     """Exposed decode time per block when block i+1 is decoded on a side stream
     while block i's seven GEMMs (torch F.linear, BF16, synthetic activations of
@@ -194,6 +278,8 @@ def main():
                     help="comma-separated batch sizes: instead of the main line, measure the decode of block i+1 "
                          "on a side stream overlapped with block i's GEMMs (one JSON line per batch)")
     ap.add_argument("--overlap-blocks", type=int, default=12)
+    ap.add_argument("--gpu-encode", action="store_true",
+                    help="instead of the main line, measure the GPU-side encoder on the workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -224,6 +310,9 @@ def main():
 
     if args.overlap:
         overlap_bench(args, dev)
+        return
+    if args.gpu_encode:
+        gpu_encode_bench(args, dev)
         return
 
     wl = di.WORKLOADS[args.workload]

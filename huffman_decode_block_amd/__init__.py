@@ -72,6 +72,16 @@ class df11_device_block(ctypes.Structure):
     ]
 
 
+class df11_gpu_plan(ctypes.Structure):
+    _fields_ = [
+        ("code_len", ctypes.c_uint8 * 256),
+        ("n_symbols", _u32), ("max_code_len", _u32), ("n_tables", _u32), ("flags", _u32),
+        ("n_total", _u64), ("total_bits", _u64), ("n_windows", _u64), ("n_units", _u64),
+        ("stream_bytes", _u64), ("sign_mant_bytes", _u64), ("gaps_bytes", _u64), ("unit_pos_bytes", _u64),
+        ("counts_bytes", _u64), ("tables_bytes", _u64), ("workspace_bytes", _u64),
+    ]
+
+
 class df11_launch(ctypes.Structure):
     _fields_ = [("waves_per_group", _u32), ("max_groups", _u32), ("variant", _u32), ("oversubscribe", _u32)]
 
@@ -94,6 +104,7 @@ EXPORTS = [
     "df11_encode_block", "df11_encode_block_ex", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
+    "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode",
 ]
 
 
@@ -124,6 +135,12 @@ def lib():
     L.df11_device_block_from_blob.restype = ctypes.c_int32
     L.df11_decode_block.argtypes = [P(df11_device_block), _vp, _u64, _vp]
     L.df11_decode_block.restype = ctypes.c_int32
+    L.df11_gpu_histogram.argtypes = [_vp, _u64, _vp, _vp]
+    L.df11_gpu_histogram.restype = ctypes.c_int32
+    L.df11_gpu_plan_build.argtypes = [_vp, _u32, P(df11_gpu_plan)]
+    L.df11_gpu_plan_build.restype = ctypes.c_int32
+    L.df11_gpu_encode.argtypes = [P(df11_gpu_plan), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.df11_gpu_encode.restype = ctypes.c_int32
     L.df11_decode_block_ex.argtypes = [P(df11_device_block), _vp, _u64, _vp, P(df11_launch)]
     L.df11_decode_block_ex.restype = ctypes.c_int32
     L.df11_status_str.argtypes = [ctypes.c_int32]
@@ -406,6 +423,92 @@ def df11_decode_block_ex(block: DeviceBlock, out=None, stream=None, waves_per_gr
     return df11_decode_block(block, out, stream, launch=(waves_per_group, max_groups, variant, oversubscribe))
 
 
+def df11_gpu_histogram(x, hist, stream=None) -> None:
+    """hist (device, 256 int64) := exponent histogram of x (16-bit device tensor)."""
+    _check(lib().df11_gpu_histogram(x.data_ptr(), x.numel(), hist.data_ptr(), _stream_handle(stream, x.device)),
+           "df11_gpu_histogram")
+
+
+def df11_gpu_plan_build(hist, flags: int = 0) -> df11_gpu_plan:
+    """The GPU encoder's plan for a host histogram (256 counts)."""
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    if h.size != 256:
+        raise ValueError("a histogram has 256 counts")
+    plan = df11_gpu_plan()
+    _check(lib().df11_gpu_plan_build(h.ctypes.data, flags, ctypes.byref(plan)), "df11_gpu_plan_build")
+    return plan
+
+
+def df11_gpu_encode(plan: df11_gpu_plan, x, stream_buf, sign_mant, gaps, unit_pos, counts, workspace,
+                    stream=None) -> None:
+    """Packs the sections of x (device) into the given device tensors (sizes from the plan)."""
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    _check(lib().df11_gpu_encode(ctypes.byref(plan), ptr(x), ptr(stream_buf), ptr(sign_mant), ptr(gaps),
+                                 ptr(unit_pos), ptr(counts), ptr(workspace), _stream_handle(stream, x.device)),
+           "df11_gpu_encode")
+
+
+class GpuEncoded:
+    """A block encoded on the device: its plan, the section tensors and a
+    DeviceBlock ready for df11_decode_block."""
+
+    def __init__(self, plan, tensors: dict, block: "DeviceBlock"):
+        self.plan = plan
+        self.tensors = tensors
+        self.block = block
+
+    def section(self, name) -> np.ndarray:
+        """Host copy of a section as bytes (stream, sign_mant, gaps, unit_pos, counts)."""
+        t = self.tensors[name]
+        return t.cpu().numpy().view(np.uint8).reshape(-1)
+
+
+def gpu_encode(x, window_counts: bool = False, stream=None, mat_offset=None) -> GpuEncoded:
+    """Encode a block whose BF16 weights are in device memory (a contiguous
+    16-bit tensor, matrices concatenated).  The histogram's 256 counts come
+    back to the host for the code lengths (this synchronizes `stream`); every
+    other step runs on the device."""
+    import torch
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous 16-bit device tensor")
+    dev = x.device
+    flat = x.reshape(-1)
+    hist = torch.empty(256, dtype=torch.int64, device=dev)
+    df11_gpu_histogram(flat, hist, stream)
+    torch.cuda.synchronize(dev)  # the counts go to the host
+    plan = df11_gpu_plan_build(hist.cpu().numpy().astype(np.uint64), DF11_ENCODE_WINDOW_COUNTS if window_counts else 0)
+    t = {
+        "stream": torch.empty(max(16, plan.stream_bytes), dtype=torch.uint8, device=dev),
+        "sign_mant": torch.empty(max(16, plan.sign_mant_bytes), dtype=torch.uint8, device=dev),
+        "gaps": torch.empty(max(16, plan.gaps_bytes), dtype=torch.uint8, device=dev),
+        "unit_pos": torch.empty(plan.n_units + 1, dtype=torch.int64, device=dev),
+        "counts": torch.empty(plan.counts_bytes, dtype=torch.uint8, device=dev) if window_counts else None,
+        "workspace": torch.empty(max(16, plan.workspace_bytes), dtype=torch.uint8, device=dev),
+    }
+    code_len = np.frombuffer(bytes(plan.code_len), dtype=np.uint8).copy()
+    tables = df11_build_tables(code_len)
+    t["tables"] = torch.from_numpy(tables.view(np.uint8).reshape(-1).copy()).to(dev)
+    df11_gpu_encode(plan, flat, t["stream"], t["sign_mant"], t["gaps"], t["unit_pos"], t["counts"],
+                    t["workspace"], stream)
+    b = df11_device_block()
+    b.tables, b.tables_bytes = t["tables"].data_ptr(), plan.tables_bytes
+    b.stream, b.stream_bytes = t["stream"].data_ptr(), plan.stream_bytes
+    b.sign_mant, b.sign_mant_bytes = t["sign_mant"].data_ptr(), plan.sign_mant_bytes
+    b.gaps, b.gaps_bytes = t["gaps"].data_ptr(), plan.gaps_bytes
+    b.unit_pos = t["unit_pos"].data_ptr()
+    b.n_total, b.total_bits, b.n_windows, b.n_units = plan.n_total, plan.total_bits, plan.n_windows, plan.n_units
+    b.version = DF11_FORMAT_VERSION
+    b.n_tables = plan.n_tables
+    b.counts = t["counts"].data_ptr() if window_counts else None
+    # the largest unit is only known from unit_pos: read it back (small)
+    torch.cuda.synchronize(dev)
+    up = t["unit_pos"].cpu().numpy().astype(np.int64)
+    b.max_unit_count = int(np.diff(up).max()) if up.size > 1 else 0
+    blk = DeviceBlock(b, [v for v in t.values() if v is not None], int(plan.n_total),
+                      None if mat_offset is None else np.asarray(mat_offset, dtype=np.int64))
+    return GpuEncoded(plan, t, blk)
+
+
 def matrix_views(out, block_or_offsets, shapes=None):
     """Per-matrix views of a decoded block output."""
     off = block_or_offsets.mat_offset if hasattr(block_or_offsets, "mat_offset") else block_or_offsets
@@ -423,6 +526,7 @@ __all__ = [
     "df11_encode_block", "df11_encode_block_ex", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
+    "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode", "gpu_encode", "GpuEncoded",
     "Encoded", "Sections",
     "DeviceBlock", "DF11Error", "matrix_views", "lib",
 ]

@@ -1,5 +1,5 @@
-"""Builds libdf11.so in-tree: host encoder with g++, the gfx950 decode kernel
-with hipcc, linked by hipcc.  Run as ``python -m huffman_decode_block_amd.build``."""
+"""Builds libdf11.so in-tree: host encoder with g++, the gfx950 decode and
+encode kernels with hipcc, linked by hipcc.  Run as ``python -m huffman_decode_block_amd.build``."""
 from __future__ import annotations
 
 import os
@@ -15,7 +15,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdf11.so")
 
 HOST_SOURCES = ["df11_encode.cpp", "df11_tables.cpp", "df11_capi.cpp"]
-HIP_SOURCES = ["df11_decode.hip"]
+HIP_SOURCES = ["df11_decode.hip", "df11_gpu_encode.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -193,6 +193,28 @@ uint32_t thread_count(uint32_t requested) {
     return h ? h : 1u;
 }
 
+df11_status code_lengths_for(const uint64_t cnt[256], uint8_t code_len[256], uint32_t *max_len,
+                             uint32_t *n_symbols, uint64_t *total_bits) {
+    uint32_t len32[256];
+    uint32_t ml = huffman_lengths(cnt, len32);
+    if (ml > DF11_MAX_CODE_LEN) {
+        if (!package_merge_lengths(cnt, DF11_MAX_CODE_LEN, len32)) return DF11_E_FORMAT;
+        ml = 0;
+        for (int e = 0; e < 256; ++e) ml = std::max(ml, len32[e]);
+    }
+    uint32_t ns = 0;
+    uint64_t tb = 0;
+    for (int e = 0; e < 256; ++e) {
+        code_len[e] = static_cast<uint8_t>(len32[e]);
+        ns += cnt[e] ? 1u : 0u;
+        tb += cnt[e] * len32[e];
+    }
+    *max_len = ml;
+    *n_symbols = ns;
+    *total_bits = tb;
+    return DF11_OK;
+}
+
 }  // namespace df11i
 
 extern "C" df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_mats,
@@ -226,21 +248,13 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
         for (int e = 0; e < 256; ++e) cnt[e] += h[e];
 
     // ---- code lengths and canonical codes
-    uint32_t len32[256];
-    uint32_t max_len = huffman_lengths(cnt, len32);
-    if (max_len > DF11_MAX_CODE_LEN) {
-        if (!package_merge_lengths(cnt, DF11_MAX_CODE_LEN, len32)) return DF11_E_FORMAT;
-        max_len = 0;
-        for (int e = 0; e < 256; ++e) max_len = std::max(max_len, len32[e]);
-    }
     uint8_t code_len[256];
-    uint32_t n_symbols = 0;
+    uint32_t max_len = 0, n_symbols = 0;
     uint64_t total_bits = 0;
-    for (int e = 0; e < 256; ++e) {
-        code_len[e] = static_cast<uint8_t>(len32[e]);
-        n_symbols += cnt[e] ? 1u : 0u;
-        total_bits += cnt[e] * len32[e];
-    }
+    if (df11i::code_lengths_for(cnt, code_len, &max_len, &n_symbols, &total_bits) != DF11_OK)
+        return DF11_E_FORMAT;
+    uint32_t len32[256];
+    for (int e = 0; e < 256; ++e) len32[e] = code_len[e];
     uint32_t code[256];
     if (!df11i::canonical_codes(code_len, code)) return DF11_E_FORMAT;
     uint32_t n_tables = 0;

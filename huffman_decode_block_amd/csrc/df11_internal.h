@@ -69,6 +69,13 @@ bool canonical_codes(const uint8_t code_len[256], uint32_t code[256]);
 // Number of host threads to use for a request (0 = all CPUs available).
 uint32_t thread_count(uint32_t requested);
 
+// Code lengths for an exponent histogram: the deterministic Huffman code,
+// length-limited to DF11_MAX_CODE_LEN by package-merge when needed (the rule
+// of df11_encode_block); also the longest code, the symbols present and the
+// stream length in bits.
+df11_status code_lengths_for(const uint64_t cnt[256], uint8_t code_len[256], uint32_t *max_len,
+                             uint32_t *n_symbols, uint64_t *total_bits);
+
 }  // namespace df11i
 
 struct df11_encoded {

@@ -236,6 +236,54 @@ df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf1
                                  uint64_t out_capacity, void *hip_stream,
                                  const df11_launch *launch);
 
+/* ---- GPU-side encoder ---------------------------------------------------
+ * The step before the decode, for a block whose BF16 weights are already in
+ * device memory: the exponent histogram is taken on the device, the host
+ * turns its 256 counts into code lengths (the same rule as
+ * df11_encode_block), and the device computes every code's bit offset by a
+ * prefix sum and packs all sections.  The sections are byte for byte those of
+ * df11_encode_block on the same weights (hada.io summary of the DFloat11
+ * paper, sections "Le format DFloat11" and "Noyau GPU en deux etapes et
+ * metadonnees auxiliaires").  All calls are stream-ordered on hip_stream
+ * (NULL = the null stream), never synchronize and allocate nothing. */
+
+/* hist[0..256) (device, uint64) := histogram of the exponents of x[0..n)
+ * (device, BF16 bit patterns, 2-byte aligned).  Errors: DF11_E_INVALID_ARG,
+ * DF11_E_HIP (launch failure). */
+df11_status df11_gpu_histogram(const uint16_t *x, uint64_t n, uint64_t *hist, void *hip_stream);
+
+/* What the GPU encoder will produce for a histogram, and the buffers it needs
+ * (bytes, caller-allocated device memory). */
+typedef struct df11_gpu_plan {
+    uint8_t code_len[256];          /* code length per exponent, 0 = absent */
+    uint32_t n_symbols, max_code_len, n_tables, flags;
+    uint64_t n_total, total_bits, n_windows, n_units;
+    uint64_t stream_bytes;          /* 512 * n_units + 16 */
+    uint64_t sign_mant_bytes;       /* n_total rounded up to 16 */
+    uint64_t gaps_bytes;            /* 40 * n_units + 8 */
+    uint64_t unit_pos_bytes;        /* 8 * (n_units + 1) */
+    uint64_t counts_bytes;          /* 64 * n_units with DF11_ENCODE_WINDOW_COUNTS, else 0 */
+    uint64_t tables_bytes;          /* df11_build_tables output for code_len */
+    uint64_t workspace_bytes;       /* device scratch for df11_gpu_encode */
+} df11_gpu_plan;
+
+/* Host: the plan for a histogram (host copy of df11_gpu_histogram's result)
+ * and encoder flags (DF11_ENCODE_WINDOW_COUNTS or 0).  Errors:
+ * DF11_E_INVALID_ARG, DF11_E_FORMAT. */
+df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t flags, df11_gpu_plan *plan);
+
+/* Encodes x[0..plan->n_total) (device) into the caller's device buffers, sized
+ * as in the plan: stream (16-byte aligned), sign_mant, gaps, unit_pos
+ * (8-byte aligned), counts (NULL unless plan->flags has
+ * DF11_ENCODE_WINDOW_COUNTS) and workspace (plan->workspace_bytes, 16-byte
+ * aligned, contents are scratch).  x must hold the weights the histogram was
+ * taken from.  The decode tables are built on the host with
+ * df11_build_tables(plan->code_len).  Errors: DF11_E_INVALID_ARG (null or
+ * misaligned pointers, flags that do not match), DF11_E_HIP. */
+df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, uint8_t *stream, uint8_t *sign_mant,
+                            uint8_t *gaps, uint64_t *unit_pos, uint8_t *counts, void *workspace,
+                            void *hip_stream);
+
 /* Text for a status code (static storage). */
 const char *df11_status_str(df11_status s);
 

@@ -1,0 +1,121 @@
+"""GPU parity of the GPU-side encoder: every section byte for byte against
+the host encoder (itself byte-for-byte equal to the oracle, see
+test_encoder_parity.py) and, for a few inputs, the oracle directly; then the
+GPU decode of the GPU-encoded block must give back the input."""
+import numpy as np
+import pytest
+
+import df11_inputs as di
+import huffman_decode_block_amd as hdb
+import oracle
+from conftest import load_golden
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "the GPU tests need a GPU"
+    return t
+
+
+def check(torch, x, name, counts=False, with_oracle=False):
+    say(f"gpu encode {name}: n={x.size} counts={counts}")
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    g = hdb.gpu_encode(xd, window_counts=counts)
+    s = hdb.df11_encode_block([x], window_counts=counts).sections
+    p = g.plan
+    assert bytes(p.code_len) == bytes(s.code_len) and p.total_bits == s.total_bits
+    np.testing.assert_array_equal(g.section("stream")[:p.stream_bytes], s.stream)
+    np.testing.assert_array_equal(g.section("sign_mant")[:p.sign_mant_bytes], s.sign_mant)
+    np.testing.assert_array_equal(g.section("gaps")[:p.gaps_bytes], s.gaps)
+    np.testing.assert_array_equal(g.section("unit_pos").view(np.uint64), s.unit_pos)
+    if counts:
+        np.testing.assert_array_equal(g.section("counts"), s.counts)
+    if with_oracle:
+        o = oracle.encode(x)
+        np.testing.assert_array_equal(g.section("stream")[:o.stream.size], o.stream)
+        np.testing.assert_array_equal(g.section("gaps")[:o.gaps.size], o.gaps)
+        np.testing.assert_array_equal(g.section("unit_pos").view(np.uint64), o.unit_pos)
+    # round trip through the GPU decoder
+    out = torch.empty(max(1, x.size), dtype=torch.bfloat16, device="cuda")
+    variants = (hdb.DF11_VARIANT_MULTI, hdb.DF11_VARIANT_COUNTS) if counts else (hdb.DF11_VARIANT_MULTI,)
+    for v in variants:
+        out.view(torch.int16).fill_(0x5A5A)
+        hdb.df11_decode_block(g.block, out=out[:x.size], launch=(0, 0, v))
+        torch.cuda.synchronize()
+        assert torch.equal(out[:x.size].view(torch.int16), xd), f"{name}: decode of the GPU encoding differs"
+    return g
+
+
+@pytest.mark.parametrize("name", ["v1_mixed_small", "v3_single_exponent", "v5_straddle_window",
+                                  "v6_last_window_without_start"])
+def test_golden_vectors(torch, name):
+    check(torch, np.array(load_golden(name)["x"], dtype=np.uint16), name, counts=True, with_oracle=True)
+
+
+@pytest.mark.parametrize("n", [1, 2, 15, 16, 17, 4095, 4096, 4097, 8193, 65_537, 262_145, 1_000_003])
+def test_ragged_sizes(torch, n):
+    check(torch, di.random_normal(n, 0.02, 700 + n), f"ragged_{n}", counts=(n % 2 == 1))
+
+
+EDGE = {
+    "all_patterns": lambda: di.all_bf16_patterns(),
+    "all_patterns_perm": lambda: di.all_bf16_patterns(5),
+    "high_exponents": lambda: di.high_exponents(100_003, 7),
+    "single_300k": lambda: di.single_exponent(300_000, 119, 4),
+    "fibonacci34_len32": lambda: di.fibonacci_exponents(),
+    "many_subtables": lambda: di.many_subtables(),
+    "skew_flat": lambda: di.skewed(400_000, 256, 0.3, 8),
+    "skew_steep": lambda: di.skewed(400_000, 12, 2.5, 9),
+    "c1": lambda: di.generate("C1"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge_inputs(torch, case):
+    check(torch, EDGE[case](), case, counts=True, with_oracle=case in ("c1", "fibonacci34_len32"))
+
+
+def test_histogram(torch):
+    x = di.generate("C2")
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    for n in (x.size, x.size - 3, 7, 0):
+        h = torch.empty(256, dtype=torch.int64, device="cuda")
+        hdb.df11_gpu_histogram(xd[:n], h)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(h.cpu().numpy(), np.bincount((x[:n] >> 7) & 0xFF, minlength=256))
+
+
+def test_workload_c2(torch):
+    check(torch, di.generate("C2"), "C2", counts=True)
+
+
+def test_workload_c3_full(torch):
+    x = di.generate("C3")
+    g = check(torch, x, "C3", counts=True)
+    assert g.plan.n_total == x.size
+
+
+def test_argument_errors(torch):
+    x = di.random_normal(10_000, 0.02, 3)
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    h = torch.empty(256, dtype=torch.int64, device="cuda")
+    with pytest.raises(hdb.DF11Error) as ei:
+        hdb.df11_gpu_histogram(xd[1:], h)  # not 16-byte aligned
+    assert ei.value.status == hdb.DF11_E_INVALID_ARG
+    plan = hdb.df11_gpu_plan_build(np.bincount((x >> 7) & 0xFF, minlength=256).astype(np.uint64))
+    buf = lambda n: torch.empty(max(16, n), dtype=torch.uint8, device="cuda")  # noqa: E731
+    args = [buf(plan.stream_bytes), buf(plan.sign_mant_bytes), buf(plan.gaps_bytes),
+            torch.empty(plan.n_units + 1, dtype=torch.int64, device="cuda")]
+    with pytest.raises(hdb.DF11Error) as ei:  # counts given, but the plan has none
+        hdb.df11_gpu_encode(plan, xd, *args, buf(64 * plan.n_units), buf(plan.workspace_bytes))
+    assert ei.value.status == hdb.DF11_E_INVALID_ARG
+    with pytest.raises(hdb.DF11Error) as ei:  # misaligned input
+        hdb.df11_gpu_encode(plan, xd[1:], *args, None, buf(plan.workspace_bytes))
+    assert ei.value.status == hdb.DF11_E_INVALID_ARG
