@@ -14,14 +14,25 @@
 //     matrix of a transformer block.
 //
 // Mapping to CDNA4: one 64-lane wavefront decodes one unit of 64 windows, so
-// the prefix sum is a wave-level scan and the stored position is per unit.
-// Waves of a workgroup share the decode tables in LDS and each owns a private
-// LDS staging area, so no workgroup barrier is needed after the tables are
-// loaded.  Workgroups are persistent (grid-stride over groups of units).
-// Staging holds the exponent already shifted into place (exponent << 7) as
-// 16-bit values; the final merge with the sign/mantissa bytes is one byte
-// permute and one bitfield insert per pair of weights, and the output goes out
-// as 16-byte stores (16-bit stores only at the two ends of a unit).
+// the prefix sum is a wave-level scan (DPP) and the stored position is per
+// unit.  Waves of a workgroup share the decode tables in LDS and each owns a
+// private LDS staging area, so no workgroup barrier is needed after the tables
+// are loaded; the grid walks groups of units with a stride (several
+// workgroups per resident slot).  Unit inputs and outputs go through buffer
+// resources (base and size in scalar registers, 32-bit lane offsets).
+//
+// Two ways to take codes from the stream, same output:
+//   one code per lookup through the hierarchical tables (the pages' design);
+//   multi-code: phase 1 counts every code that ends in the next 10 bits with
+//   one lookup (count table), phase 2 takes up to four codes per lookup of
+//   the next 11 bits (emit table); longer codes fall back to the hierarchical
+//   tables.  A variant reads stored per-window counts instead of phase 1.
+// Staging holds each exponent already shifted into place (exponent << 7) as a
+// 16-bit slot; the multi-code phase 2 ORs whole table entries into zeroed,
+// 8-byte-aligned staging words (unaligned LDS writes stall the LDS pipe).
+// The merge with the sign/mantissa bytes is one byte permute and one bitfield
+// insert per pair of weights, and the output goes out as 16-byte
+// non-temporal stores (16-bit stores only at the two ends of a unit).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
