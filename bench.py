@@ -73,16 +73,43 @@ def algorithmic_bytes(s, with_counts: bool = False) -> dict:
     return {"read": int(rd), "write": int(wr), "total": int(rd + wr)}
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on this workload and the current kernel code; else None."""
     if not os.path.exists(COUNTERS):
         return None
     with open(COUNTERS) as f:
         c = json.load(f)
-    if c.get("kernel_code_sha256_16") != kernel_hash():
+    if c.get("kernel_code_sha256_16") != kernel_hash() or not c.get("workload", "").startswith(workload + ":"):
         return None
     return c.get("hbm_bytes_per_launch")
+
+
+def progress(msg: str) -> None:
+    """A progress line on stderr (stdout carries only the result line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copy_context(n_bytes: int, dev, reps: int = 20) -> dict:
+    """A plain device-to-device copy that moves the same HBM bytes as one
+    decode (half read, half written), timed the same way: the achievable
+    streaming rate on this GPU, reported as context for the decode's rate."""
+    import torch
+    half = max(16, n_bytes // 2 // 16 * 16)
+    src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(5):
+        dst.copy_(src)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev[0].record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
+    del src, dst
+    return {"bytes": 2 * half, "copy_us": round(t * 1e6, 2), "copy_GBps": round(2 * half / t / 1e9, 1)}
 
 
 def cpu_baseline(sections, x, min_seconds: float) -> dict:
@@ -342,10 +369,14 @@ def main():
         return
 
     wl = di.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
     x = di.generate(args.workload)
+    progress(f"{args.workload}: {x.size:,} weights generated in {time.perf_counter() - t_gen:.1f} s")
     with_counts = args.variant == hdb.DF11_VARIANT_COUNTS
+    t_enc = time.perf_counter()
     enc = hdb.df11_encode_block(di.split(args.workload, x), window_counts=with_counts)
     s = enc.sections
+    progress(f"encoded on the host in {time.perf_counter() - t_enc:.1f} s")
     blk = hdb.DeviceBlock.from_encoded(enc, device=dev)
     out = torch.empty(s.n_total, dtype=torch.bfloat16, device=dev)
     launch = (args.waves, args.max_groups, args.variant, args.oversubscribe) \
@@ -359,6 +390,7 @@ def main():
     if not torch.equal(out.view(torch.int16), xd):
         raise SystemExit("decode is not bit-exact; refusing to report a number")
     del xd
+    progress("decode checked bit-exact; timing")
     region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -402,7 +434,9 @@ def main():
     achieved = ab["total"] / k_avg / 1e9
     value = 2.0 * n * args.steps / wall / 1e9
     # the committed counters were taken on the default (multi-code) kernel
-    traffic = measured_traffic() if args.variant in (0, 2) else None
+    traffic = measured_traffic(args.workload) if args.variant in (0, 2) else None
+    cc = copy_context(ab["total"], dev)
+    cc["decode_over_copy"] = round(achieved / cc["copy_GBps"], 3)
     res = {
         "metric": "decoded BF16 GB/s and % HBM roofline per transformer block, 1 MI355X",
         "value": round(value, 2),
@@ -450,9 +484,11 @@ def main():
             "algorithmic_bytes_per_launch": ab["total"],
             "kernel": "df11_decode_kernel",
         },
+        "copy_context": cc,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
+        progress("timing the oracle on the host (cpu_baseline)")
         res["cpu_baseline"] = cpu_baseline(s, x, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
