@@ -683,7 +683,12 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     // 8-output chunks, plus one 8-byte word that the multi-code path may OR
     // past its last slot
     const uint32_t stage_elems = static_cast<uint32_t>((blk->max_unit_count + 7 + 7) / 8 * 8 + 8);
-    auto lds_for = [&](uint32_t w) { return lds_tables * 1024u + w * stage_elems * 2u; };
+    // The merge reads whole passes of 64 chunks (up to staged slot 2,047),
+    // also past the end of a small unit's staging; the values read there are
+    // never stored, and this pad keeps the last wave's such reads inside the
+    // workgroup's LDS.
+    const uint32_t pad = stage_elems * 2u < 4096u ? 4096u - stage_elems * 2u : 0u;
+    auto lds_for = [&](uint32_t w) { return lds_tables * 1024u + w * stage_elems * 2u + pad; };
     uint32_t waves = 0, per_cu = 0;
     for (uint32_t w = 16; w >= 1; w >>= 1) {  // the geometry with the most resident waves
         if (asked && w != asked) continue;
