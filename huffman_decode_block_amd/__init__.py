@@ -104,7 +104,7 @@ EXPORTS = [
     "df11_encode_block", "df11_encode_block_ex", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
-    "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode",
+    "df11_gpu_chunk_hist_bytes", "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode",
 ]
 
 
@@ -135,11 +135,13 @@ def lib():
     L.df11_device_block_from_blob.restype = ctypes.c_int32
     L.df11_decode_block.argtypes = [P(df11_device_block), _vp, _u64, _vp]
     L.df11_decode_block.restype = ctypes.c_int32
-    L.df11_gpu_histogram.argtypes = [_vp, _u64, _vp, _vp]
+    L.df11_gpu_chunk_hist_bytes.argtypes = [_u64]
+    L.df11_gpu_chunk_hist_bytes.restype = _u64
+    L.df11_gpu_histogram.argtypes = [_vp, _u64, _vp, _vp, _vp]
     L.df11_gpu_histogram.restype = ctypes.c_int32
     L.df11_gpu_plan_build.argtypes = [_vp, _u32, P(df11_gpu_plan)]
     L.df11_gpu_plan_build.restype = ctypes.c_int32
-    L.df11_gpu_encode.argtypes = [P(df11_gpu_plan), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.df11_gpu_encode.argtypes = [P(df11_gpu_plan), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.df11_gpu_encode.restype = ctypes.c_int32
     L.df11_decode_block_ex.argtypes = [P(df11_device_block), _vp, _u64, _vp, P(df11_launch)]
     L.df11_decode_block_ex.restype = ctypes.c_int32
@@ -423,9 +425,17 @@ def df11_decode_block_ex(block: DeviceBlock, out=None, stream=None, waves_per_gr
     return df11_decode_block(block, out, stream, launch=(waves_per_group, max_groups, variant, oversubscribe))
 
 
-def df11_gpu_histogram(x, hist, stream=None) -> None:
-    """hist (device, 256 int64) := exponent histogram of x (16-bit device tensor)."""
-    _check(lib().df11_gpu_histogram(x.data_ptr(), x.numel(), hist.data_ptr(), _stream_handle(stream, x.device)),
+def df11_gpu_chunk_hist_bytes(n: int) -> int:
+    """Bytes of the per-chunk exponent counts of n weights (256 uint16 per 4,096 weights)."""
+    return int(lib().df11_gpu_chunk_hist_bytes(int(n)))
+
+
+def df11_gpu_histogram(x, hist, chunk_hist=None, stream=None) -> None:
+    """hist (device, 256 int64) := exponent histogram of x (16-bit device
+    tensor); chunk_hist (device, df11_gpu_chunk_hist_bytes(x.numel()) bytes, or
+    None) := the 256 counts of every chunk of 4,096 weights, as uint16."""
+    ptr = None if chunk_hist is None else chunk_hist.data_ptr()
+    _check(lib().df11_gpu_histogram(x.data_ptr(), x.numel(), hist.data_ptr(), ptr, _stream_handle(stream, x.device)),
            "df11_gpu_histogram")
 
 
@@ -439,12 +449,15 @@ def df11_gpu_plan_build(hist, flags: int = 0) -> df11_gpu_plan:
     return plan
 
 
-def df11_gpu_encode(plan: df11_gpu_plan, x, stream_buf, sign_mant, gaps, unit_pos, counts, workspace,
+def df11_gpu_encode(plan: df11_gpu_plan, x, chunk_hist, stream_buf, sign_mant, gaps, unit_pos, counts, workspace,
                     stream=None) -> None:
-    """Packs the sections of x (device) into the given device tensors (sizes from the plan)."""
+    """Packs the sections of x (device) into the given device tensors (sizes
+    from the plan); chunk_hist holds the per-chunk counts df11_gpu_histogram
+    took from the same x."""
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    _check(lib().df11_gpu_encode(ctypes.byref(plan), ptr(x), ptr(stream_buf), ptr(sign_mant), ptr(gaps),
-                                 ptr(unit_pos), ptr(counts), ptr(workspace), _stream_handle(stream, x.device)),
+    _check(lib().df11_gpu_encode(ctypes.byref(plan), ptr(x), ptr(chunk_hist), ptr(stream_buf), ptr(sign_mant),
+                                 ptr(gaps), ptr(unit_pos), ptr(counts), ptr(workspace),
+                                 _stream_handle(stream, x.device)),
            "df11_gpu_encode")
 
 
@@ -474,7 +487,8 @@ def gpu_encode(x, window_counts: bool = False, stream=None, mat_offset=None) -> 
     dev = x.device
     flat = x.reshape(-1)
     hist = torch.empty(256, dtype=torch.int64, device=dev)
-    df11_gpu_histogram(flat, hist, stream)
+    chunk_hist = torch.empty(max(8, df11_gpu_chunk_hist_bytes(flat.numel()) // 2), dtype=torch.int16, device=dev)
+    df11_gpu_histogram(flat, hist, chunk_hist, stream)
     torch.cuda.synchronize(dev)  # the counts go to the host
     plan = df11_gpu_plan_build(hist.cpu().numpy().astype(np.uint64), DF11_ENCODE_WINDOW_COUNTS if window_counts else 0)
     t = {
@@ -484,11 +498,12 @@ def gpu_encode(x, window_counts: bool = False, stream=None, mat_offset=None) -> 
         "unit_pos": torch.empty(plan.n_units + 1, dtype=torch.int64, device=dev),
         "counts": torch.empty(plan.counts_bytes, dtype=torch.uint8, device=dev) if window_counts else None,
         "workspace": torch.empty(max(16, plan.workspace_bytes), dtype=torch.uint8, device=dev),
+        "chunk_hist": chunk_hist,
     }
     code_len = np.frombuffer(bytes(plan.code_len), dtype=np.uint8).copy()
     tables = df11_build_tables(code_len)
     t["tables"] = torch.from_numpy(tables.view(np.uint8).reshape(-1).copy()).to(dev)
-    df11_gpu_encode(plan, flat, t["stream"], t["sign_mant"], t["gaps"], t["unit_pos"], t["counts"],
+    df11_gpu_encode(plan, flat, chunk_hist, t["stream"], t["sign_mant"], t["gaps"], t["unit_pos"], t["counts"],
                     t["workspace"], stream)
     b = df11_device_block()
     b.tables, b.tables_bytes = t["tables"].data_ptr(), plan.tables_bytes
@@ -526,7 +541,8 @@ __all__ = [
     "df11_encode_block", "df11_encode_block_ex", "df11_encoded_sections", "df11_encoded_free", "df11_validate",
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
-    "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode", "gpu_encode", "GpuEncoded",
+    "df11_gpu_chunk_hist_bytes", "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode", "gpu_encode",
+    "GpuEncoded",
     "Encoded", "Sections",
     "DeviceBlock", "DF11Error", "matrix_views", "lib",
 ]

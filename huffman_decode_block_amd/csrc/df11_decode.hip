@@ -39,6 +39,7 @@
 #include <mutex>
 
 #include "df11_internal.h"
+#include "df11_wave.h"
 
 namespace {
 
@@ -106,23 +107,6 @@ __device__ __forceinline__ void consume(uint32_t e, uint32_t &h, uint32_t &l, ui
     h = __builtin_amdgcn_alignbit(h, l, e);
     l = __builtin_amdgcn_alignbit(l, r, e);
     r = __builtin_amdgcn_alignbit(r, 0u, e);
-}
-
-// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
-// broadcasts (cross-lane moves inside the VALU, no LDS round trip):
-// shifts by 1, 2, 3 then 4 and 8 give the scan within each row of 16 lanes;
-// broadcasting lane 15 into rows 1 and 3, then lane 31 into rows 2 and 3,
-// carries the row totals across.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-    uint32_t s = x;
-    s += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);  // row_shr:1
-    s += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);  // row_shr:2
-    s += __builtin_amdgcn_update_dpp(0u, x, 0x113, 0xF, 0xF, true);  // row_shr:3
-    s += __builtin_amdgcn_update_dpp(0u, s, 0x114, 0xF, 0xE, false); // row_shr:4, lanes 4..15 of a row
-    s += __builtin_amdgcn_update_dpp(0u, s, 0x118, 0xF, 0xC, false); // row_shr:8, lanes 8..15 of a row
-    s += __builtin_amdgcn_update_dpp(0u, s, 0x142, 0xA, 0xF, false); // row_bcast:15 into rows 1, 3
-    s += __builtin_amdgcn_update_dpp(0u, s, 0x143, 0xC, 0xF, false); // row_bcast:31 into rows 2, 3
-    return s;
 }
 
 // Two BF16 values from two staged (exponent << 7) halves and the sign/mantissa
@@ -306,20 +290,12 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
 __shared__ __align__(16) uint32_t s_count_table[df11i::kCountEntries];
 __shared__ __align__(16) uint2 s_emit_table[df11i::kEmitEntries];
 
-// Buffer resources: a base address and a size in scalar registers, accessed
-// with 32-bit per-lane offsets.  Loads past the size return 0 and stores past
-// it are dropped, so masked accesses need an out-of-range offset rather than
-// a branch.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-constexpr uint32_t kOff = 0x80000000u;  // an offset past every resource used here
-constexpr int kNonTemporal = 2;        // cache policy bit of buffer accesses: non-temporal
-
-__device__ __forceinline__ Rsrc rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
-                                             static_cast<int>(bytes), 0x00020000);
-}
+using df11w::kNonTemporal;
+using df11w::kOff;
+using df11w::rsrc;
+using df11w::Rsrc;
+using df11w::v2u;
+using df11w::v4u;
 
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
@@ -437,7 +413,7 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     }
 
     // ---- wave prefix sum of the counts
-    const uint32_t excl = wave_inclusive_scan(cnt) - cnt;
+    const uint32_t excl = df11w::wave_inclusive_scan(cnt) - cnt;
 
     // ---- phase 2: decode again, stage (exponent << 7) at the output slot
     const uint32_t first = lead + excl;

@@ -247,10 +247,19 @@ df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf1
  * metadonnees auxiliaires").  All calls are stream-ordered on hip_stream
  * (NULL = the null stream), never synchronize and allocate nothing. */
 
+/* Bytes of the per-chunk histograms of n weights: 256 uint16 counts for each
+ * chunk of 4,096 weights (the last chunk may be shorter). */
+uint64_t df11_gpu_chunk_hist_bytes(uint64_t n);
+
 /* hist[0..256) (device, uint64) := histogram of the exponents of x[0..n)
- * (device, BF16 bit patterns, 2-byte aligned).  Errors: DF11_E_INVALID_ARG,
- * DF11_E_HIP (launch failure). */
-df11_status df11_gpu_histogram(const uint16_t *x, uint64_t n, uint64_t *hist, void *hip_stream);
+ * (device, BF16 bit patterns, 16-byte aligned); and, when chunk_hist is not
+ * NULL, chunk_hist (device, df11_gpu_chunk_hist_bytes(n) bytes, 16-byte
+ * aligned) := for every chunk of 4,096 weights its 256 exponent counts.
+ * df11_gpu_encode takes the chunk counts, so that it does not read the
+ * weights a second time to size each chunk's codes.  Errors:
+ * DF11_E_INVALID_ARG, DF11_E_HIP (launch failure). */
+df11_status df11_gpu_histogram(const uint16_t *x, uint64_t n, uint64_t *hist, uint16_t *chunk_hist,
+                               void *hip_stream);
 
 /* What the GPU encoder will produce for a histogram, and the buffers it needs
  * (bytes, caller-allocated device memory). */
@@ -273,16 +282,17 @@ typedef struct df11_gpu_plan {
 df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t flags, df11_gpu_plan *plan);
 
 /* Encodes x[0..plan->n_total) (device) into the caller's device buffers, sized
- * as in the plan: stream (16-byte aligned), sign_mant, gaps, unit_pos
- * (8-byte aligned), counts (NULL unless plan->flags has
+ * as in the plan: stream (16-byte aligned), sign_mant (16-byte aligned), gaps,
+ * unit_pos (8-byte aligned), counts (NULL unless plan->flags has
  * DF11_ENCODE_WINDOW_COUNTS) and workspace (plan->workspace_bytes, 16-byte
- * aligned, contents are scratch).  x must hold the weights the histogram was
- * taken from.  The decode tables are built on the host with
+ * aligned, contents are scratch).  x and chunk_hist must be the weights and
+ * the per-chunk counts df11_gpu_histogram took the plan's histogram from.
+ * The decode tables are built on the host with
  * df11_build_tables(plan->code_len).  Errors: DF11_E_INVALID_ARG (null or
  * misaligned pointers, flags that do not match), DF11_E_HIP. */
-df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, uint8_t *stream, uint8_t *sign_mant,
-                            uint8_t *gaps, uint64_t *unit_pos, uint8_t *counts, void *workspace,
-                            void *hip_stream);
+df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint16_t *chunk_hist,
+                            uint8_t *stream, uint8_t *sign_mant, uint8_t *gaps, uint64_t *unit_pos,
+                            uint8_t *counts, void *workspace, void *hip_stream);
 
 /* Text for a status code (static storage). */
 const char *df11_status_str(df11_status s);

@@ -47,6 +47,13 @@ def test_kernel_hash_is_stable_under_comment_edits(bench, tmp_path, monkeypatch)
     assert bench.kernel_hash() == h
     f.write_text(src + "\nint extra_symbol;\n")
     assert bench.kernel_hash() != h
+    # the included headers are part of the identity
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(tmp_path / "k.hip"))
+    f.write_text(src)
+    hdr = tmp_path / "w.h"
+    hdr.write_text(open(bench.KERNEL_HEADERS[0]).read() + "\nint other;\n")
+    monkeypatch.setattr(bench, "KERNEL_HEADERS", [str(hdr)])
+    assert bench.kernel_hash() != h
 
 
 def test_measured_traffic_only_for_matching_code_and_workload(bench, tmp_path, monkeypatch):

@@ -85,11 +85,22 @@ def test_edge_inputs(torch, case):
 def test_histogram(torch):
     x = di.generate("C2")
     xd = torch.from_numpy(x.view(np.int16)).to("cuda")
-    for n in (x.size, x.size - 3, 7, 0):
+    for n in (x.size, x.size - 3, 4096 * 37 + 1, 4095, 7, 0):
         h = torch.empty(256, dtype=torch.int64, device="cuda")
-        hdb.df11_gpu_histogram(xd[:n], h)
+        nb = hdb.df11_gpu_chunk_hist_bytes(n)
+        assert nb == 512 * ((n + 4095) // 4096)
+        ch = torch.full((max(8, nb // 2),), -1, dtype=torch.int16, device="cuda")
+        hdb.df11_gpu_histogram(xd[:n], h, ch)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(h.cpu().numpy(), np.bincount((x[:n] >> 7) & 0xFF, minlength=256))
+        e = (x[:n] >> 7) & 0xFF
+        np.testing.assert_array_equal(h.cpu().numpy(), np.bincount(e, minlength=256))
+        got = ch.cpu().numpy().view(np.uint16)[:nb // 2].reshape(-1, 256)
+        for c in range(got.shape[0]):
+            np.testing.assert_array_equal(got[c], np.bincount(e[4096 * c:4096 * (c + 1)], minlength=256))
+        h2 = torch.empty(256, dtype=torch.int64, device="cuda")
+        hdb.df11_gpu_histogram(xd[:n], h2)  # without the per-chunk counts
+        torch.cuda.synchronize()
+        assert torch.equal(h, h2)
 
 
 def test_workload_c2(torch):
@@ -109,13 +120,22 @@ def test_argument_errors(torch):
     with pytest.raises(hdb.DF11Error) as ei:
         hdb.df11_gpu_histogram(xd[1:], h)  # not 16-byte aligned
     assert ei.value.status == hdb.DF11_E_INVALID_ARG
+    ch = torch.empty(hdb.df11_gpu_chunk_hist_bytes(x.size) // 2 + 8, dtype=torch.int16, device="cuda")
+    with pytest.raises(hdb.DF11Error) as ei:
+        hdb.df11_gpu_histogram(xd, h, ch[1:])  # per-chunk counts not 16-byte aligned
+    assert ei.value.status == hdb.DF11_E_INVALID_ARG
+    hdb.df11_gpu_histogram(xd, h, ch)
+    torch.cuda.synchronize()
     plan = hdb.df11_gpu_plan_build(np.bincount((x >> 7) & 0xFF, minlength=256).astype(np.uint64))
     buf = lambda n: torch.empty(max(16, n), dtype=torch.uint8, device="cuda")  # noqa: E731
     args = [buf(plan.stream_bytes), buf(plan.sign_mant_bytes), buf(plan.gaps_bytes),
             torch.empty(plan.n_units + 1, dtype=torch.int64, device="cuda")]
     with pytest.raises(hdb.DF11Error) as ei:  # counts given, but the plan has none
-        hdb.df11_gpu_encode(plan, xd, *args, buf(64 * plan.n_units), buf(plan.workspace_bytes))
+        hdb.df11_gpu_encode(plan, xd, ch, *args, buf(64 * plan.n_units), buf(plan.workspace_bytes))
     assert ei.value.status == hdb.DF11_E_INVALID_ARG
     with pytest.raises(hdb.DF11Error) as ei:  # misaligned input
-        hdb.df11_gpu_encode(plan, xd[1:], *args, None, buf(plan.workspace_bytes))
+        hdb.df11_gpu_encode(plan, xd[1:], ch, *args, None, buf(plan.workspace_bytes))
+    assert ei.value.status == hdb.DF11_E_INVALID_ARG
+    with pytest.raises(hdb.DF11Error) as ei:  # no per-chunk counts
+        hdb.df11_gpu_encode(plan, xd, None, *args, None, buf(plan.workspace_bytes))
     assert ei.value.status == hdb.DF11_E_INVALID_ARG
