@@ -37,10 +37,11 @@
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint32_t kPerThread = 16;                   // weights per thread in hist/pack
+constexpr uint32_t kPerThread = 16;                   // weights per thread in hist
 constexpr uint32_t kChunk = kThreads * kPerThread;    // 4,096 weights per chunk
-constexpr uint32_t kBitWords = kChunk * 32 / 32 + 2;  // LDS words for a chunk's codes
 constexpr uint32_t kSegChunks = kThreads;             // chunks per segment of the two-level scan
+constexpr uint32_t kPackThreads = 512;                // pack: threads per workgroup
+constexpr uint32_t kPackPer = kChunk / kPackThreads;  // pack: weights per thread (8)
 constexpr uint32_t kScanThreads = 1024;
 
 struct EncParams {
@@ -140,41 +141,41 @@ __global__ void __launch_bounds__(kThreads) fill_kernel(EncParams p) {
     }
 }
 
-// Weights of thread t of chunk c, sixteen as eight packed words (two weights
-// each, the first in the low half).  load_full requests them for a whole
-// chunk (a chunk that is not whole reads as zeros, through a buffer range of
-// 0 bytes) and does not use them, so that the loads stay in flight;
+// Weights of pack thread t of chunk c, eight as four packed words (two
+// weights each, the first in the low half).  load_full requests them for a
+// whole chunk (a chunk that is not whole reads as zeros, through a buffer
+// range of 0 bytes) and does not use them, so that the loads stay in flight;
 // load_partial reads the block's last, partial chunk element by element.
 __device__ __forceinline__ bool chunk_is_full(const EncParams &p, uint64_t c) { return (c + 1) * kChunk <= p.n; }
 
-__device__ __forceinline__ void load_full(const EncParams &p, uint64_t c, uint32_t t, uint32_t w[8]) {
+__device__ __forceinline__ void load_full(const EncParams &p, uint64_t c, uint32_t t, uint32_t w[4]) {
     const bool full = chunk_is_full(p, c);
     const df11w::Rsrc r = df11w::rsrc(p.x + (full ? c * kChunk : 0), full ? 2 * kChunk : 0u);
-    const df11w::v4u a = __builtin_amdgcn_raw_buffer_load_b128(r, 32 * t, 0, 0);
-    const df11w::v4u b = __builtin_amdgcn_raw_buffer_load_b128(r, 32 * t + 16, 0, 0);
-    w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w, w[4] = b.x, w[5] = b.y, w[6] = b.z, w[7] = b.w;
+    const df11w::v4u a = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * t, 0, 0);
+    w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w;
 }
 
 __device__ __forceinline__ void load_partial(const EncParams &p, uint64_t c, uint32_t t, uint32_t m,
-                                             uint32_t w[8]) {
-    const uint64_t i0 = c * kChunk + uint64_t{t} * kPerThread;
+                                             uint32_t w[4]) {
+    const uint64_t i0 = c * kChunk + uint64_t{t} * kPackPer;
 #pragma unroll
-    for (uint32_t k = 0; k < 8; ++k) {
+    for (uint32_t k = 0; k < 4; ++k) {
         const uint32_t lo = 2 * k < m ? p.x[i0 + 2 * k] : 0u;
         const uint32_t hi = 2 * k + 1 < m ? p.x[i0 + 2 * k + 1] : 0u;
         w[k] = lo | (hi << 16);
     }
 }
 
-// Weights of chunk c that thread t takes (0..16).
+// Weights of chunk c that pack thread t takes (0..8).
 __device__ __forceinline__ uint32_t weights_of(const EncParams &p, uint64_t c, uint32_t t) {
-    const uint64_t i0 = c * kChunk + uint64_t{t} * kPerThread;
-    return i0 >= p.n ? 0u : static_cast<uint32_t>(p.n - i0 < kPerThread ? p.n - i0 : kPerThread);
+    const uint64_t i0 = c * kChunk + uint64_t{t} * kPackPer;
+    return i0 >= p.n ? 0u : static_cast<uint32_t>(p.n - i0 < kPackPer ? p.n - i0 : kPackPer);
 }
 
-// Block-wide exclusive sum of one value per thread (256 threads = 4 waves):
-// a scan inside each wave, then each wave adds the totals of the waves before
-// it; also the block total.  `wsum` holds 4 values.
+// Block-wide exclusive sum of one value per thread (kWaves waves): a scan
+// inside each wave, then each wave adds the totals of the waves before it;
+// also the block total.  `wsum` holds kWaves values.
+template <uint32_t kWaves>
 __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *wsum, uint32_t &total) {
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     const uint32_t incl = df11w::wave_inclusive_scan(v);
@@ -183,7 +184,7 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *ws
     uint32_t before = 0;
     total = 0;
 #pragma unroll
-    for (uint32_t k = 0; k < kThreads / 64; ++k) {
+    for (uint32_t k = 0; k < kWaves; ++k) {
         const uint32_t w = wsum[k];
         before += k < wave ? w : 0u;
         total += w;
@@ -214,7 +215,7 @@ __global__ void __launch_bounds__(kThreads) bits_kernel(EncParams p) {
         }
     }
     uint32_t seg_bits;
-    const uint32_t pre = block_exclusive_sum(bits, wsum, seg_bits);
+    const uint32_t pre = block_exclusive_sum<kThreads / 64>(bits, wsum, seg_bits);
     if (c < p.n_chunks) p.chunk_pre[c] = pre;
     if (t == 0) p.seg_sum[blockIdx.x] = seg_bits;
 }
@@ -248,167 +249,207 @@ __global__ void __launch_bounds__(kScanThreads) top_kernel(EncParams p) {
 // ---------------------------------------------------------------- pack
 // Persistent: each workgroup takes chunks c, c + grid, ... and requests the
 // next chunk's weights before packing the current one.  Per chunk, thread t
-// takes weights 16t .. 16t + 15: their codes form one run of bits that starts
+// takes weights 8t .. 8t + 7: their codes form one run of bits that starts
 // at the chunk's offset plus the block prefix of the threads' run lengths.
 //
-// First-start records (the gap of every window, the first weight of every
-// unit, and with window counts the first weight of every window): a code is
-// the first to start in its window when the code before it started in an
-// earlier window.  Each thread decides this for its codes 1..15 and, at the
-// end of its run, for the code that follows it (the next thread's or next
-// chunk's first), which it knows to start where its own run ends; the
-// block's very first code is the first of window 0 and unit 0.
-constexpr uint32_t kChunkWindows = kChunk * 32 / 64 + 2;  // windows a chunk's records can fall in
-constexpr uint8_t kNoStart = 0xFF;                          // a window without a record here
+// LDS frame: bit positions count from the start of the 64-bit window that
+// holds the chunk's first code, so a 32-bit word index serves the code
+// buffer and the code-start bitmap alike, and windows are word pairs.
+//
+// First-start records come from the bitmap: a window's gap is the position of
+// its first set bit, the first weight of the window is the chunk's first
+// weight plus the starts before it (prefix of popcounts), and a window that
+// opens a unit (64 windows) gives that unit's position.  A window belongs to
+// the chunk that holds its first start: the chunk's first window is left to
+// the previous chunk when that one's last code starts in it.
+// 32-bit words of a chunk's frame: at most 63 + 32 x 4,096 bits, the word after
+// the last one a code reaches, whole windows; a multiple of 4
+constexpr uint32_t kFrameWords = kChunk + 4;
+constexpr uint32_t kWinPerThread = (kFrameWords / 2 + kPackThreads - 1) / kPackThreads;
 
-__global__ void __launch_bounds__(kThreads) pack_kernel(EncParams p) {
+__device__ __forceinline__ uint32_t clz64(uint64_t v) { return v ? static_cast<uint32_t>(__clzll(v)) : 64u; }
+
+// What the loop requests for the next chunk while packing the current one.
+// The loaded values are not combined here: any use makes the wave wait.
+struct ChunkInputs {
+    uint32_t w[4];      // the thread's eight weights, packed
+    uint64_t seg_off;   // the chunk's first bit is seg_off + pre
+    uint32_t pre;
+    uint32_t x_last;    // the previous chunk's last weight (chunk 0: not used)
+};
+
+// A load through the scalar data cache (read only): the address is the same
+// for the whole wave, and the wait for it (lgkmcnt) is not ordered with the
+// vector memory stores in flight.
+template <class T>
+__device__ __forceinline__ T scalar_load(const T *ptr) {
+    return *(const __attribute__((address_space(4))) T *)(ptr);
+}
+
+__device__ __forceinline__ void load_inputs(const EncParams &p, uint64_t c, uint32_t t, ChunkInputs &in) {
+    const uint64_t cc = c < p.n_chunks ? c : 0;  // past the end: chunk 0 again, not used
+    in.seg_off = scalar_load(p.seg_off + cc / kSegChunks);
+    in.pre = scalar_load(p.chunk_pre + cc);
+    // the 4-byte word whose high half is the previous chunk's last weight
+    // (chunk 0: any readable word, not used)
+    const uint32_t *wl = cc ? reinterpret_cast<const uint32_t *>(p.x + cc * kChunk - 2) : p.chunk_pre;
+    in.x_last = scalar_load(wl) >> 16;
+    load_full(p, c, t, in.w);
+}
+
+// Packs chunk c.  Its stores of the code words and window records come after
+// `next` is taken (its loads were requested before this chunk's work, so
+// they have arrived): vmcnt counts loads and stores in issue order, and a wait
+// for the next chunk's loads after these stores would also wait for them.
+template <bool kWhole>
+__device__ __forceinline__ void pack_chunk(const EncParams &p, uint64_t c, const ChunkInputs &in,
+                                           const ChunkInputs &next, const uint2 *ent, uint32_t *bits,
+                                           uint32_t *starts, uint32_t *wsum, uint32_t *wsum2) {
+    const uint32_t t = threadIdx.x;
+    const uint64_t i0 = c * kChunk + uint64_t{t} * kPackPer;
+    const uint32_t m = kWhole ? kPackPer : weights_of(p, c, t);
+    const uint32_t *wc = in.w;
+    const uint64_t cb = in.seg_off + in.pre;
+    const uint32_t len_last = ent[exponent_of(in.x_last)].y;
+
+    // sign/mantissa bytes, (sign << 7) | mantissa, two weights per word
+    uint32_t smw[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t a = wc[2 * k], b = wc[2 * k + 1];
+        const uint32_t sa = ((a >> 8) & 0x00800080u) | (a & 0x007F007Fu);  // two sm bytes in 16-bit halves
+        const uint32_t sb = ((b >> 8) & 0x00800080u) | (b & 0x007F007Fu);
+        smw[k] = __builtin_amdgcn_perm(sb, sa, 0x06040200u);
+    }
+    if (kWhole || m == kPackPer) {
+        reinterpret_cast<uint2 *>(p.sm + i0)[0] = make_uint2(smw[0], smw[1]);
+    } else {
+        for (uint32_t k = 0; k < m; ++k) p.sm[i0 + k] = static_cast<uint8_t>(smw[k / 4] >> (8 * (k & 3)));
+    }
+
+    // codes and lengths of the thread's weights (length 0 past the end)
+    uint32_t code[kPackPer], len[kPackPer];
+    uint32_t sum = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kPackPer; ++k) {
+        const uint2 e = ent[exponent_of(wc[k / 2] >> (16 * (k & 1)))];
+        code[k] = (kWhole || k < m) ? e.x : 0u;
+        len[k] = (kWhole || k < m) ? e.y : 0u;
+        sum += len[k];
+    }
+
+    // this thread's first bit in the frame
+    uint32_t chunk_bits;
+    const uint32_t pre = block_exclusive_sum<kPackThreads / 64>(sum, wsum, chunk_bits);
+    const uint32_t head = static_cast<uint32_t>(cb & 63u);
+
+    // Each code is ORed into the code buffer at its own position (one 64-bit
+    // shift, two 32-bit ORs: the word it starts in and the next) and its
+    // start into the bitmap, so that no thread waits on another's words.
+    uint32_t pos = head + pre;
+#pragma unroll
+    for (uint32_t k = 0; k < kPackPer; ++k) {
+        const uint32_t l = len[k];
+        const uint32_t wi = pos >> 5, sh = pos & 31u;
+        const uint64_t v = static_cast<uint64_t>(code[k]) << ((64u - sh - l) & 63u);
+        atomicOr(&bits[wi], static_cast<uint32_t>(v >> 32));
+        atomicOr(&bits[wi + 1], static_cast<uint32_t>(v));
+        if (kWhole || k < m) atomicOr(&starts[wi], 0x80000000u >> sh);
+        pos += l;
+    }
+    lds_barrier();
+    asm volatile("" ::"v"(next.w[0]), "v"(next.w[1]), "v"(next.w[2]), "v"(next.w[3]));
+
+    // out to HBM as big-endian words, clearing the buffer for the next chunk;
+    // the first and last words are shared with the neighbouring chunks when
+    // the chunk does not start or end on a word boundary
+    const uint32_t k0 = head >> 5;
+    const uint32_t nwords = (head + chunk_bits + 31u) >> 5;
+    const bool head_shared = (cb & 31u) != 0;
+    const bool tail_shared = ((cb + chunk_bits) & 31u) != 0;
+    uint32_t *out = reinterpret_cast<uint32_t *>(p.stream) + 2 * (cb >> 6);
+    const uint64_t room = p.stream_bytes / 4 > 2 * (cb >> 6) ? p.stream_bytes / 4 - 2 * (cb >> 6) : 0;
+    for (uint32_t k = k0 + t; k < nwords; k += blockDim.x) {
+        const uint32_t v = __builtin_bswap32(bits[k]);
+        bits[k] = 0;
+        if (k >= room) continue;
+        if ((k == k0 && head_shared) || (k == nwords - 1 && tail_shared))
+            atomicOr(out + k, v);
+        else
+            out[k] = v;
+    }
+
+    // window records: thread t takes windows t*q .. t*q + q - 1 of the
+    // chunk's nwin, counts the starts in each, and the block scan of the
+    // counts gives every window the starts before it
+    const uint64_t wbase = cb >> 6;
+    const uint32_t nwin = (head + chunk_bits + 63u) >> 6;
+    const uint32_t q = (nwin + kPackThreads - 1) / kPackThreads;
+    const uint32_t jb = t * q;
+    uint64_t wv[kWinPerThread];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < kWinPerThread; ++i) {
+        const uint32_t j = jb + i;
+        wv[i] = 0;
+        if (i < q && j < nwin) {
+            wv[i] = (static_cast<uint64_t>(starts[2 * j]) << 32) | starts[2 * j + 1];
+            starts[2 * j] = 0;
+            starts[2 * j + 1] = 0;
+            cnt += static_cast<uint32_t>(__popcll(wv[i]));
+        }
+    }
+    uint32_t total;
+    uint32_t before = block_exclusive_sum<kPackThreads / 64>(cnt, wsum2, total);
+    const bool prev_has_start = c > 0 && head >= len_last;  // the previous chunk's last code starts in window 0
+#pragma unroll
+    for (uint32_t i = 0; i < kWinPerThread; ++i) {
+        const uint32_t j = jb + i;
+        const uint64_t w = wbase + j;
+        if (wv[i] && (j > 0 || !prev_has_start) && w < p.n_windows) {
+            const uint64_t first = c * kChunk + before;  // the window's first weight
+            p.gap8[w] = static_cast<uint8_t>(clz64(wv[i]));
+            if (p.wfirst) p.wfirst[w] = first;
+            if ((w & 63u) == 0) p.unit_pos[w >> 6] = first;
+        }
+        before += static_cast<uint32_t>(__popcll(wv[i]));
+    }
+}
+
+__global__ void __launch_bounds__(kPackThreads) pack_kernel(EncParams p) {
     __shared__ uint2 ent[256];  // per exponent: code, length
-    __shared__ __align__(16) uint32_t bits[kBitWords + 2];
-    __shared__ uint32_t wsum[kThreads / 64];
-    // window records of the chunk, from its first code's window on: the gap,
-    // and the first weight's offset from the chunk's first weight
-    __shared__ uint8_t gap_l[kChunkWindows];
-    __shared__ uint16_t wfirst_l[kChunkWindows];
+    __shared__ __align__(16) uint32_t bits[kFrameWords];
+    __shared__ __align__(16) uint32_t starts[kFrameWords];
+    __shared__ uint32_t wsum[kPackThreads / 64], wsum2[kPackThreads / 64];
     const uint32_t t = threadIdx.x;
     uint64_t c = blockIdx.x;
     if (c >= p.n_chunks) return;  // uniform
-    ent[t] = make_uint2(p.code[t], p.len[t]);
-    for (uint32_t k = t; k < (kBitWords + 2) / 4; k += blockDim.x)
+    if (t < 256) ent[t] = make_uint2(p.code[t], p.len[t]);
+    for (uint32_t k = t; k < kFrameWords / 4; k += blockDim.x) {
         reinterpret_cast<uint4 *>(bits)[k] = make_uint4(0u, 0u, 0u, 0u);
-    for (uint32_t k = t; k < kChunkWindows; k += blockDim.x) gap_l[k] = kNoStart;
-    uint32_t wc[8];
-    load_full(p, c, t, wc);
-    lds_barrier();
-    if (c == 0 && t == 0) {  // the block's first code starts at bit 0
-        p.gap8[0] = 0;
-        if (p.wfirst) p.wfirst[0] = 0;
-        p.unit_pos[0] = 0;
+        reinterpret_cast<uint4 *>(starts)[k] = make_uint4(0u, 0u, 0u, 0u);
     }
+    ChunkInputs cur;
+    load_inputs(p, c, t, cur);
+    // the first chunk's inputs before the loop: its head then sees them
+    // complete, with no wait that would also drain the stores
+    asm volatile("" ::"v"(cur.w[0]), "v"(cur.w[1]), "v"(cur.w[2]), "v"(cur.w[3]));
+    lds_barrier();
 
     while (true) {
-        const uint64_t cb = p.seg_off[c / kSegChunks] + p.chunk_pre[c];
-        // the next chunk's weights, requested a whole chunk ahead
+        // the next chunk's inputs, requested a whole chunk ahead
         const uint64_t cn = c + gridDim.x;
-        uint32_t wn[8];
-        load_full(p, cn, t, wn);
-        const uint64_t i0 = c * kChunk + uint64_t{t} * kPerThread;
-        const uint32_t m = weights_of(p, c, t);
-        if (!chunk_is_full(p, c)) load_partial(p, c, t, m, wc);  // the block's last chunk (uniform)
-
-        // sign/mantissa bytes, (sign << 7) | mantissa, two weights per word
-        if (m == kPerThread) {
-            uint32_t v[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t a = wc[2 * k], b = wc[2 * k + 1];
-                const uint32_t sa = ((a >> 8) & 0x00800080u) | (a & 0x007F007Fu);  // two sm bytes in 16-bit halves
-                const uint32_t sb = ((b >> 8) & 0x00800080u) | (b & 0x007F007Fu);
-                v[k] = __builtin_amdgcn_perm(sb, sa, 0x06040200u);
-            }
-            reinterpret_cast<uint4 *>(p.sm + i0)[0] = make_uint4(v[0], v[1], v[2], v[3]);
-        } else {
-            for (uint32_t k = 0; k < m; ++k) {
-                const uint32_t x = (wc[k / 2] >> (16 * (k & 1))) & 0xFFFFu;
-                p.sm[i0 + k] = static_cast<uint8_t>(((x >> 8) & 0x80u) | (x & 0x7Fu));
-            }
-        }
-
-        // codes and lengths of the thread's weights (length 0 past the end)
-        uint32_t code[kPerThread], len[kPerThread];
-        uint32_t sum = 0;
-#pragma unroll
-        for (uint32_t k = 0; k < kPerThread; ++k) {
-            const uint2 e = ent[exponent_of(wc[k / 2] >> (16 * (k & 1)))];
-            code[k] = k < m ? e.x : 0u;
-            len[k] = k < m ? e.y : 0u;
-            sum += len[k];
-        }
-
-        // this thread's first bit: chunk offset + block prefix of the run lengths
-        uint32_t chunk_bits;
-        const uint32_t pre = block_exclusive_sum(sum, wsum, chunk_bits);
-        const uint64_t b0 = cb + pre;
-        const uint32_t lb = static_cast<uint32_t>(cb & 31u) + pre;  // bit index in the LDS buffer
-
-        // Each code is ORed into the LDS bit buffer at its own position (one
-        // 64-bit shift, two 32-bit ORs: the word it starts in and the next),
-        // so that no thread waits on another's words and no branch is taken
-        // per code.  Lengths past the block's end are 0, their codes 0.
-        //
-        // First-start rules in 32-bit arithmetic: a code's start is kept as
-        // b0's offset in its window plus 64 plus the lengths before it (at
-        // most 512 bits on): the window index changes exactly when the bits
-        // from 6 up differ from the previous code's start.  Unit starts are
-        // window starts; the unit rule is checked only for those.
-        const uint64_t lim64 = p.total_bits > b0 ? p.total_bits - b0 : 0;
-        const uint32_t lim = lim64 < 0xFFFFFFFFull ? static_cast<uint32_t>(lim64) : 0xFFFFFFFFu;
-        const uint32_t rw = static_cast<uint32_t>(b0 & 63u) + 64u;
-        const uint32_t ru = static_cast<uint32_t>(b0 & 4095u) + 4096u;
-        const uint64_t w0 = (b0 >> 6) - 1, u0 = (b0 >> 12) - 1;  // window/unit index of a biased 0
-        const uint64_t wbase = cb >> 6;  // the chunk's first window
-        const uint32_t wl0 = static_cast<uint32_t>(w0 - wbase);  // w0 + x is window wbase + wl0 + x
-        auto record = [&](uint32_t cw, uint32_t cwp, uint32_t j) {  // code c * 4096 + j starts at biased cw
-            const uint32_t o = cw - rw;
-            if (((cw ^ cwp) >= 64u) && o < lim) {  // the first code to start in its window
-                const uint32_t wl = wl0 + (cw >> 6);
-                gap_l[wl] = static_cast<uint8_t>(cw & 63u);
-                wfirst_l[wl] = static_cast<uint16_t>(j);
-                const uint32_t cu = ru + o, pu = ru + (cwp - rw);
-                if ((cu >> 12) != (pu >> 12)) p.unit_pos[u0 + (cu >> 12)] = c * kChunk + j;  // and in its unit
-            }
-        };
-        // Code k's rule runs at step k (k >= 1); the code after the run is
-        // decided at step m when the run is short (the block's end: steps past
-        // it see equal starts and record nothing), else after the last step.
-        uint32_t pos = lb;    // LDS bit position of code k
-        uint32_t cw = rw;     // biased start of code k
-        uint32_t cwp = rw;    // biased start of code k - 1
-#pragma unroll
-        for (uint32_t k = 0; k < kPerThread; ++k) {
-            const uint32_t l = len[k];
-            if (k > 0) record(cw, cwp, t * kPerThread + k);
-            const uint64_t v = static_cast<uint64_t>(code[k]) << ((64u - (pos & 31u) - l) & 63u);
-            atomicOr(&bits[pos >> 5], static_cast<uint32_t>(v >> 32));
-            atomicOr(&bits[(pos >> 5) + 1], static_cast<uint32_t>(v));
-            cwp = cw;
-            cw += l;
-            pos += l;
-        }
-        if (m == kPerThread) record(cw, cwp, t * kPerThread + kPerThread);  // the code after the run
-        lds_barrier();
-
-        // out to HBM as big-endian words, clearing the buffer for the next
-        // chunk; the first and last words are shared with the neighbouring
-        // chunks when the chunk is not word-aligned there
-        const uint32_t head = static_cast<uint32_t>(cb & 31u);
-        const uint32_t nwords = (head + chunk_bits + 31u) >> 5;
-        const bool tail_shared = ((cb + chunk_bits) & 31u) != 0;
-        uint32_t *out = reinterpret_cast<uint32_t *>(p.stream) + (cb >> 5);
-        const uint64_t room = p.stream_bytes / 4 > (cb >> 5) ? p.stream_bytes / 4 - (cb >> 5) : 0;
-        for (uint32_t k = t; k < nwords; k += blockDim.x) {
-            const uint32_t v = __builtin_bswap32(bits[k]);
-            bits[k] = 0;
-            if (k >= room) continue;
-            if ((k == 0 && head) || (k == nwords - 1 && tail_shared))
-                atomicOr(out + k, v);
-            else
-                out[k] = v;
-        }
-        // the window records, from the chunk's first window to the window of
-        // the next chunk's first code (clearing them for the next chunk)
-        const uint32_t nwin = static_cast<uint32_t>(((cb + chunk_bits) >> 6) - wbase) + 1;
-        for (uint32_t k = t; k < nwin; k += blockDim.x) {
-            const uint32_t g = gap_l[k];
-            if (g == kNoStart) continue;
-            gap_l[k] = kNoStart;
-            if (wbase + k >= p.n_windows) continue;
-            p.gap8[wbase + k] = static_cast<uint8_t>(g);
-            if (p.wfirst) p.wfirst[wbase + k] = c * kChunk + wfirst_l[k];
+        ChunkInputs nxt;
+        load_inputs(p, cn, t, nxt);
+        if (chunk_is_full(p, c)) {  // uniform
+            pack_chunk<true>(p, c, cur, nxt, ent, bits, starts, wsum, wsum2);
+        } else {  // the block's last chunk
+            load_partial(p, c, t, weights_of(p, c, t), cur.w);
+            pack_chunk<false>(p, c, cur, nxt, ent, bits, starts, wsum, wsum2);
         }
         if (cn >= p.n_chunks) break;  // uniform
         c = cn;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) wc[k] = wn[k];
+        cur = nxt;  // arrived: taken before this chunk's stores
     }
 }
 
@@ -482,7 +523,7 @@ uint32_t pack_groups() {
         cus = 256;
     }
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&pack_kernel),
-                                                     static_cast<int>(kThreads), 0) != hipSuccess ||
+                                                     static_cast<int>(kPackThreads), 0) != hipSuccess ||
         per_cu < 1) {
         (void)hipGetLastError();
         per_cu = 4;
@@ -601,7 +642,7 @@ extern "C" df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t
     if (err == hipSuccess && chunks) {
         // a few workgroups per resident slot: enough to fill the GPU, each
         // taking many chunks so that the next chunk's loads overlap the current
-        err = launch(pack_kernel, std::min<uint32_t>(chunks, pack_groups()), kThreads, st, p);
+        err = launch(pack_kernel, std::min<uint32_t>(chunks, pack_groups()), kPackThreads, st, p);
     }
     if (err == hipSuccess && nw) err = launch(finish_kernel, grid_for(nw / 8 + 1, 4096), kThreads, st, p);
     if (err != hipSuccess) {
