@@ -18,7 +18,11 @@ Parity status: every function here is pinned by the not-gpu tests (round
 trip on all BF16 patterns, Kraft equality, entropy bound, brute-force and
 dynamic-programming optimality, hand-derived vectors, vectorised
 re-derivation of gaps and positions, a bit-by-bit walk of each window for the
-per-window counts).
+per-window counts; for the aligned-units variant a closed-form layout, the
+round trip, its invariants and the gap rule re-applied to the pages' format).
+
+Two format variants that are not on the pages are defined here in numpy
+(`window_counts`, `encode_aligned_units`); everything else is the C file.
 """
 from __future__ import annotations
 
@@ -146,6 +150,7 @@ class Encoded:
     gaps: np.ndarray          # uint8[40*n_units + 8]
     unit_pos: np.ndarray      # uint64[n_units + 1]
     max_len: int
+    unit_end: np.ndarray | None = None  # aligned-units variant: uint16[n_units], bits of codes per unit
 
 
 def encode(x) -> Encoded:
@@ -219,6 +224,103 @@ def decode_units(enc: Encoded, u_begin: int = 0, u_end: int | None = None,
     return out
 
 
+UNIT_BITS = 4096   # 64 windows of 64 bits: one stored position per unit
+GROUP = 32         # aligned-units variant: codes per group (64 output bytes)
+
+
+def code_starts(enc: Encoded, decoded=None) -> np.ndarray:
+    """Stream bit at which each weight's codeword starts: the lengths of the
+    codes before it, plus, in the aligned-units variant, the filler bits before
+    it (the layout rule of `aligned_layout`)."""
+    x = decode_units(enc) if decoded is None else _u16(decoded)
+    lengths = enc.code_len.astype(np.int64)[(x >> 7) & 0xFF]
+    if enc.unit_end is not None:
+        return aligned_layout(lengths)[0]
+    if not x.size:
+        return np.zeros(0, np.int64)
+    return np.concatenate([np.zeros(1, np.int64), np.cumsum(lengths)[:-1]])
+
+
+def aligned_layout(lengths) -> tuple:
+    """Code starts of the aligned-units variant (ours, not the pages'): the
+    codes are taken in groups of 32 consecutive weights, in order.  A group is
+    placed right after the previous one unless one of its codes would then
+    start in a later unit than its first code (a unit being 4,096 stream bits);
+    in that case the rest of the current unit is left as zero filler and the
+    group starts at the next unit's first bit.  So every unit but the last
+    holds a whole number of groups, and the first weight of every unit is a
+    multiple of 32.  Returns (starts int64[n], unit code ends int64[n_units]
+    (absolute: the filler's first bit, the unit's end when it has none, and
+    the stream's end for the last unit), total stream bits)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    n = lengths.size
+    starts = np.zeros(n, np.int64)
+    ends = {}  # unit -> absolute end of its codes, where a filler follows
+    pos = 0
+    for g0 in range(0, n, GROUP):
+        glen = lengths[g0:g0 + GROUP]
+        offs = np.concatenate([np.zeros(1, np.int64), np.cumsum(glen)[:-1]])
+        u = pos // UNIT_BITS
+        if pos + offs[-1] >= (u + 1) * UNIT_BITS:  # its last code would start in the next unit
+            ends[u] = pos
+            pos = (u + 1) * UNIT_BITS
+        starts[g0:g0 + glen.size] = pos + offs
+        pos += int(glen.sum())
+    total_bits = pos
+    n_units = ((total_bits + 63) // 64 + 63) // 64
+    unit_end = np.array([ends.get(u, min((u + 1) * UNIT_BITS, total_bits)) for u in range(n_units)],
+                        dtype=np.int64)
+    return starts, unit_end, total_bits
+
+
+def encode_aligned_units(x) -> Encoded:
+    """The aligned-units format variant (ours, not the pages'): code lengths,
+    codewords and sign/mantissa bytes as in `encode`; the codes laid out by
+    `aligned_layout`, filler bits 0.  Gaps: for window w of unit u, the first
+    code start at or after 64w, or the end of u's codes if none comes before
+    it, minus 64w (0 for a window entirely past the end of u's codes).  Unit
+    positions: the number of codes that start before the unit.  unit_end[u]:
+    the end of u's codes minus the unit's first bit.  The first weight of
+    every unit is then a multiple of 32, so a decoder's writes of consecutive
+    units meet on 64-byte boundaries."""
+    base = encode(x)
+    xs = _u16(x)
+    codes = canonical_codes(base.code_len.astype(np.uint32)).astype(np.int64)
+    lengths = base.code_len.astype(np.int64)[(xs >> 7) & 0xFF]
+    starts, ends_abs, total_bits = aligned_layout(lengths)
+    n_windows = (total_bits + 63) // 64
+    n_units = (n_windows + 63) // 64
+    # stream: codeword bits MSB-first at their starts, everything else 0
+    bits = np.zeros(8 * (512 * n_units + 16), dtype=np.uint8)
+    if xs.size:
+        cw = codes[(xs >> 7) & 0xFF]
+        rep = np.repeat(np.arange(xs.size), lengths)
+        j = np.arange(rep.size) - np.repeat(np.cumsum(lengths) - lengths, lengths)  # bit index in its code
+        bits[starts[rep] + j] = ((cw[rep] >> (lengths[rep] - 1 - j)) & 1).astype(np.uint8)
+    stream = np.packbits(bits)
+    # gaps
+    w = np.arange(n_windows, dtype=np.int64)
+    end_w = ends_abs[w // 64]
+    if starts.size:
+        nxt = np.searchsorted(starts, 64 * w)  # first code starting at or after 64w
+        first = np.where(nxt < starts.size, starts[np.minimum(nxt, starts.size - 1)], total_bits)
+    else:
+        first = np.full(n_windows, total_bits, dtype=np.int64)
+    gap = np.where(64 * w >= end_w, 0, np.minimum(first, end_w) - 64 * w)
+    assert (gap >= 0).all() and (gap <= 31).all()
+    gbits = np.zeros(8 * (40 * n_units + 8), dtype=np.uint8)  # 5-bit fields, MSB-first
+    for k in range(5):
+        gbits[5 * w + k] = (gap >> (4 - k)) & 1
+    gaps = np.packbits(gbits)[:40 * n_units + 8]
+    unit_pos = np.zeros(n_units + 1, dtype=np.uint64)
+    unit_pos[:n_units] = np.searchsorted(starts, UNIT_BITS * np.arange(n_units, dtype=np.int64))
+    unit_pos[n_units] = xs.size
+    unit_end = (ends_abs - UNIT_BITS * np.arange(n_units, dtype=np.int64)).astype(np.uint16)
+    return Encoded(n=xs.size, total_bits=int(total_bits), n_windows=int(n_windows), n_units=int(n_units),
+                   code_len=base.code_len, stream=stream, sign_mant=base.sign_mant, gaps=gaps,
+                   unit_pos=unit_pos, max_len=base.max_len, unit_end=unit_end)
+
+
 def window_counts(enc: Encoded, decoded=None) -> np.ndarray:
     """Per-window code counts of a format variant that is not on the pages:
     for each 64-bit window w, the number of codewords whose first bit lies in
@@ -227,12 +329,9 @@ def window_counts(enc: Encoded, decoded=None) -> np.ndarray:
     metadonnees auxiliaires"), this is exactly the count of codes starting in
     [64w + gap_w, min(64w + 64, total_bits)), the number that the decoder's
     first phase computes for the window.  Code starts come from the oracle's
-    own decode of the stream (or `decoded`, its result, when already at hand):
-    start_i = sum of the code lengths of the exponents before i.  Returns
-    n_windows uint8 values (each at most 64)."""
-    x = decode(enc) if decoded is None else _u16(decoded)
-    lengths = enc.code_len.astype(np.int64)[(x >> 7) & 0xFF]
-    starts = np.concatenate([np.zeros(1, np.int64), np.cumsum(lengths)[:-1]]) if x.size else np.zeros(0, np.int64)
+    own decode of the stream (or `decoded`, its result, when already at hand)
+    through `code_starts`.  Returns n_windows uint8 values (each at most 64)."""
+    starts = code_starts(enc, decoded)
     counts = np.bincount(starts >> 6, minlength=enc.n_windows)[:enc.n_windows]
     return counts.astype(np.uint8)
 
