@@ -74,7 +74,8 @@ def algorithmic_bytes(s, with_counts: bool = False) -> dict:
           + (5 * s.n_windows + 7) // 8     # 5-bit gaps
           + 8 * (s.n_units + 1)            # unit positions
           + s.raw.tables_bytes             # decode tables
-          + (s.n_windows if with_counts else 0))  # per-window counts (counting-free variant)
+          + (s.n_windows if with_counts else 0)  # per-window counts (counting-free variant)
+          + 2 * (s.n_units if s.unit_end is not None else 0))  # unit ends (aligned-units layout)
     wr = 2 * s.n_total
     return {"read": int(rd), "write": int(wr), "total": int(rd + wr)}
 
@@ -328,6 +329,9 @@ def main():
     ap.add_argument("--variant", type=int, default=0,
                     help="1 = one code per lookup, 2 = multi-code lookups (0 = library default), "
                          "3 = multi-code with stored per-window counts (a format variant)")
+    ap.add_argument("--aligned-units", action="store_true",
+                    help="encode with the aligned-units layout (a format variant: units start on "
+                         "32-weight boundaries)")
     ap.add_argument("--prewarm-ms", type=float, default=500.0,
                     help="untimed decodes before the warmup steps, for this long (the GPU's clocks ramp up "
                          "over the first ~10 ms of load after host-side work)")
@@ -380,7 +384,8 @@ def main():
     progress(f"{args.workload}: {x.size:,} weights generated in {time.perf_counter() - t_gen:.1f} s")
     with_counts = args.variant == hdb.DF11_VARIANT_COUNTS
     t_enc = time.perf_counter()
-    enc = hdb.df11_encode_block(di.split(args.workload, x), window_counts=with_counts)
+    enc = hdb.df11_encode_block(di.split(args.workload, x), window_counts=with_counts,
+                                aligned_units=args.aligned_units)
     s = enc.sections
     progress(f"encoded on the host in {time.perf_counter() - t_enc:.1f} s")
     blk = hdb.DeviceBlock.from_encoded(enc, device=dev)
@@ -440,7 +445,7 @@ def main():
     achieved = ab["total"] / k_avg / 1e9
     value = 2.0 * n * args.steps / wall / 1e9
     # the committed counters were taken on the default (multi-code) kernel
-    traffic = measured_traffic(args.workload) if args.variant in (0, 2) else None
+    traffic = measured_traffic(args.workload) if args.variant in (0, 2) and not args.aligned_units else None
     cc = copy_context(ab["total"], dev)
     cc["decode_over_copy"] = round(achieved / cc["copy_GBps"], 3)
     res = {
@@ -472,7 +477,8 @@ def main():
                        "oversubscribe": args.oversubscribe or "default",
                        "variant": {0: "default (multi-code)", 1: "one code per lookup",
                                    2: "multi-code",
-                                   3: "multi-code with stored per-window counts (format variant)"}[args.variant]},
+                                   3: "multi-code with stored per-window counts (format variant)"}[args.variant],
+                       "layout": "aligned units (format variant)" if args.aligned_units else "the pages' format"},
         },
         "gweights_per_s": round(n * args.steps / wall / 1e9, 2),
         "pct_hbm_roofline": round(100.0 * ab["total"] * args.steps / wall / 1e9 / PEAK_HBM_GBS, 2),

@@ -55,6 +55,7 @@ class df11_sections(ctypes.Structure):
         ("off_sign_mant", _u64), ("off_gaps", _u64), ("off_unit_pos", _u64), ("off_tables", _u64),
         ("exp_entropy_bits", ctypes.c_double), ("mean_code_len_bits", ctypes.c_double),
         ("counts", _vp), ("counts_bytes", _u64), ("off_counts", _u64),
+        ("unit_end", _vp), ("unit_end_bytes", _u64), ("off_unit_end", _u64),
     ]
 
 
@@ -69,6 +70,7 @@ class df11_device_block(ctypes.Structure):
         ("max_unit_count", _u64),
         ("version", _u32), ("n_tables", _u32),
         ("counts", _vp),
+        ("unit_end", _vp),
     ]
 
 
@@ -90,6 +92,7 @@ DF11_VARIANT_SINGLE = 1
 DF11_VARIANT_MULTI = 2
 DF11_VARIANT_COUNTS = 3
 DF11_ENCODE_WINDOW_COUNTS = 1
+DF11_ENCODE_ALIGNED_UNITS = 2
 
 
 class DF11Error(RuntimeError):
@@ -231,12 +234,15 @@ class Sections:
         self.blob = _np_view(s.blob, s.blob_bytes, np.uint8)
         # optional per-window code counts (64 * n_units bytes), else None
         self.counts = _np_view(s.counts, s.counts_bytes, np.uint8) if s.counts_bytes else None
+        # aligned-units layout: where each unit's codes end, from its first bit; else None
+        self.unit_end = _np_view(s.unit_end, s.n_units, np.uint16) if s.unit_end_bytes else None
 
     @property
     def compressed_bytes(self) -> int:
-        """Bytes a decode reads: stream, sign/mantissa, gaps, positions, tables."""
+        """Bytes a decode reads: stream, sign/mantissa, gaps, positions, tables
+        (and the unit ends of the aligned-units layout)."""
         return int(self.raw.stream_bytes + self.raw.sign_mant_bytes + self.raw.gaps_bytes
-                   + 8 * (self.n_units + 1) + self.raw.tables_bytes)
+                   + 8 * (self.n_units + 1) + self.raw.tables_bytes + self.raw.unit_end_bytes)
 
 
 class Encoded:
@@ -266,26 +272,28 @@ class Encoded:
         self.free()
 
 
-def df11_encode_block(mats, n_threads: int = 0, window_counts: bool = False) -> Encoded:
+def df11_encode_block(mats, n_threads: int = 0, window_counts: bool = False, aligned_units: bool = False) -> Encoded:
     """Encode a list of BF16 matrices (host) as one block with one codebook;
-    window_counts adds the per-window code counts (df11_encode_block_ex with
-    DF11_ENCODE_WINDOW_COUNTS)."""
+    window_counts adds the per-window code counts and aligned_units lays the
+    codes out so that units start on 32-weight boundaries (df11_encode_block_ex
+    with DF11_ENCODE_WINDOW_COUNTS / DF11_ENCODE_ALIGNED_UNITS)."""
+    flags = (DF11_ENCODE_WINDOW_COUNTS if window_counts else 0) | (DF11_ENCODE_ALIGNED_UNITS if aligned_units else 0)
+    return df11_encode_block_ex(mats, n_threads, flags)
+
+
+def df11_encode_block_ex(mats, n_threads: int = 0, flags: int = 0) -> Encoded:
     arrays = [_as_u16(m) for m in mats]
     views = (df11_bf16_view * max(1, len(arrays)))()
     for i, a in enumerate(arrays):
         views[i].data = a.ctypes.data if a.size else None
         views[i].numel = a.size
     h = _vp()
-    if window_counts:
-        _check(lib().df11_encode_block_ex(views, len(arrays), n_threads, DF11_ENCODE_WINDOW_COUNTS,
-                                          ctypes.byref(h)), "df11_encode_block_ex")
+    if flags:
+        _check(lib().df11_encode_block_ex(views, len(arrays), n_threads, flags, ctypes.byref(h)),
+               "df11_encode_block_ex")
     else:
         _check(lib().df11_encode_block(views, len(arrays), n_threads, ctypes.byref(h)), "df11_encode_block")
     return Encoded(h.value)
-
-
-def df11_encode_block_ex(mats, n_threads: int = 0, flags: int = 0) -> Encoded:
-    return df11_encode_block(mats, n_threads, window_counts=bool(flags & DF11_ENCODE_WINDOW_COUNTS))
 
 
 def df11_encoded_sections(enc: Encoded) -> Sections:
@@ -344,10 +352,11 @@ class DeviceBlock:
 
     @classmethod
     def from_parts(cls, *, code_len, stream, sign_mant, gaps, unit_pos, n_total, total_bits,
-                   counts=None, device="cuda") -> "DeviceBlock":
+                   counts=None, unit_end=None, device="cuda") -> "DeviceBlock":
         """Device block from separately given host sections (for example the
         oracle's); the decode tables are built here from code_len.  counts:
-        optional per-window code counts (padded here to 64 per unit)."""
+        optional per-window code counts (padded here to 64 per unit);
+        unit_end: the unit ends of the aligned-units layout."""
         import torch
         tables = df11_build_tables(code_len)
         _, n_tables = df11_tables_size(code_len)
@@ -360,6 +369,8 @@ class DeviceBlock:
             c = np.zeros(64 * nu, dtype=np.uint8)
             c[:len(counts)] = np.asarray(counts, dtype=np.uint8)[:64 * nu]
             arrays.append(("counts", c))
+        if unit_end is not None:
+            arrays.append(("unit_end", np.ascontiguousarray(unit_end, dtype=np.uint16)))
         for name, arr in arrays:
             a = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
             t = torch.empty(max(1, a.size), dtype=torch.uint8, device=device)
@@ -381,6 +392,7 @@ class DeviceBlock:
         b.version = DF11_FORMAT_VERSION
         b.n_tables = n_tables
         b.counts = parts["counts"][0].data_ptr() if "counts" in parts else None
+        b.unit_end = parts["unit_end"][0].data_ptr() if "unit_end" in parts else None
         return cls(b, [t for t, _ in parts.values()], n_total)
 
     def compressed_bytes(self) -> int:

@@ -39,7 +39,10 @@ extern "C" df11_status df11_validate(const df11_sections *s) {
     if (s->stream_bytes < 512 * nu + 16 || s->gaps_bytes < 40 * nu + 8 ||
         s->sign_mant_bytes < (s->n_total + 15) / 16 * 16)
         return DF11_E_FORMAT;
-    if (s->total_bits < s->n_total || s->total_bits > uint64_t{DF11_MAX_CODE_LEN} * s->n_total)
+    const bool aligned = s->unit_end_bytes != 0;
+    // filler (aligned units) adds at most the rest of a unit to the codes
+    if (s->total_bits < s->n_total ||
+        s->total_bits > (aligned ? 2u : 1u) * uint64_t{DF11_MAX_CODE_LEN} * s->n_total)
         return DF11_E_FORMAT;
     // code lengths: a prefix code of at most 32 bits; tables match them
     uint32_t code[256];
@@ -66,11 +69,30 @@ extern "C" df11_status df11_validate(const df11_sections *s) {
         mu = std::max(mu, d);
     }
     if (mu != s->max_unit_count) return DF11_E_FORMAT;
-    // gaps: the first code of a window starts inside it (or is the end)
+    // aligned units: unit ends within their units (the last one at the
+    // stream's end), units beginning on multiples of 32 weights, zero filler
+    if (aligned) {
+        if (!s->unit_end || s->unit_end_bytes < 2 * nu) return DF11_E_FORMAT;
+        for (uint64_t u = 0; u < nu; ++u) {
+            const uint64_t ue = s->unit_end[u];
+            if (ue < 1 || ue > 4096 || s->unit_pos[u] % 32 != 0) return DF11_E_FORMAT;
+            if (u + 1 == nu ? 4096 * u + ue != s->total_bits : false) return DF11_E_FORMAT;
+            if (u + 1 < nu)
+                for (uint64_t b = 4096 * u + ue; b < 4096 * (u + 1); ++b)
+                    if ((s->stream[b >> 3] >> (7 - (b & 7))) & 1u) return DF11_E_FORMAT;
+        }
+    }
+    // gaps: the first code of a window starts inside it, or is the end of the
+    // codes of its unit (aligned units: a window wholly past it has gap 0)
     for (uint64_t w = 0; w < nw; ++w) {
-        const uint64_t start = 64 * w + gap_field(s->gaps, w);
-        if (start > s->total_bits) return DF11_E_FORMAT;
-        if (start == s->total_bits && w + 1 != nw) return DF11_E_FORMAT;
+        const uint64_t g = gap_field(s->gaps, w), start = 64 * w + g;
+        const uint64_t end = aligned ? 4096 * (w / 64) + s->unit_end[w / 64] : s->total_bits;
+        if (aligned && 64 * w >= end) {
+            if (g != 0) return DF11_E_FORMAT;
+            continue;
+        }
+        if (start > end) return DF11_E_FORMAT;
+        if (!aligned && start == end && w + 1 != nw) return DF11_E_FORMAT;
     }
     // optional per-window counts: at most 64 each, summing to each unit's count
     if (s->counts_bytes) {
@@ -110,6 +132,7 @@ extern "C" df11_status df11_device_block_from_blob(const df11_sections *s, const
     d.version = s->version;
     d.n_tables = s->n_tables;
     d.counts = s->counts_bytes ? b + s->off_counts : nullptr;
+    d.unit_end = s->unit_end_bytes ? reinterpret_cast<const uint16_t *>(b + s->off_unit_end) : nullptr;
     *out = d;
     return DF11_OK;
 }

@@ -53,6 +53,7 @@ struct KParams {
     const uint8_t *gaps;
     const uint64_t *unit_pos;
     const uint8_t *counts;  // per-window code counts (the counting-free variant only)
+    const uint16_t *unit_end;  // per unit, where its codes end (aligned-units layout), or null
     uint16_t *out;
     uint64_t n_total, total_bits, n_windows, n_units;
     uint32_t last_unit_bits;  // stream bits in the last unit (1..4096)
@@ -318,6 +319,7 @@ __device__ __forceinline__ uint64_t lane_u64(uint64_t v, uint32_t k) {
 struct UnitInputs {
     uint32_t w0, w1, w2, g0, g1;
     uint32_t c;    // the window's stored code count (counting-free variant)
+    uint32_t ue;   // where the unit's codes end (aligned-units layout; 0 otherwise)
     uint64_t pos;  // unit_pos[u] in even lanes, unit_pos[u + 1] in odd lanes
 };
 
@@ -335,6 +337,9 @@ __device__ __forceinline__ void load_unit(const KParams &p, uint64_t u, uint32_t
     const v2u q = __builtin_amdgcn_raw_buffer_load_b64(up, 8 * (lane & 1), 0, 0);
     in.pos = (static_cast<uint64_t>(q.y) << 32) | q.x;
     in.c = kCounts ? __builtin_amdgcn_raw_buffer_load_b8(rsrc(p.counts + 64 * u, 64), lane, 0, 0) : 0u;
+    // a range of 0 bytes (reads 0) when the block has no unit ends
+    const Rsrc ur = p.unit_end ? rsrc(p.unit_end + u, 2) : rsrc(p.unit_pos, 0);
+    in.ue = __builtin_amdgcn_raw_buffer_load_b16(ur, 0, 0, 0);
 }
 
 constexpr uint32_t kChunksPerPass = 64;  // 8-output chunks, one per lane
@@ -387,7 +392,8 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     }
 
     // ---- this lane's window: gap and end (bits of the stream left in it)
-    const uint32_t ulim = u == p.n_units - 1 ? p.last_unit_bits : 4096u;
+    const uint32_t ulim = p.unit_end ? __builtin_amdgcn_readfirstlane(in.ue)
+                                     : u == p.n_units - 1 ? p.last_unit_bits : 4096u;
     const int end = min(max(static_cast<int>(ulim) - 64 * static_cast<int>(lane), 0), 64);
     const uint32_t gap2 = (in.g0 << 8) | in.g1;  // big-endian 16 bits
     const uint32_t gap = (gap2 >> (11u - ((5 * lane) & 7))) & 31u;
@@ -457,7 +463,7 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     // loads, so they have arrived; taking them here keeps the copy into the
     // current set (after the stores) from waiting on the stores.
     asm volatile("" ::"v"(next.w0), "v"(next.w1), "v"(next.w2), "v"(next.g0), "v"(next.g1), "v"(next.pos),
-                 "v"(next.c), "v"(eout));
+                 "v"(next.c), "v"(next.ue), "v"(eout));
 #pragma unroll
     for (int k = 0; k < 3; ++k) put_chunk(lane + kChunksPerPass * k, outv[k]);
     if (pass3) put_chunk(lane + kChunksPerPass * 3, outv[3]);
@@ -516,7 +522,7 @@ df11_decode_kernel(KParams p) {
         if (__syncthreads_or(bad)) return;
     }
 
-    const uint32_t lane = threadIdx.x & 63u;
+    uint32_t lane = threadIdx.x & 63u;
     // wave index and wave count are uniform: keep unit indices in scalar registers
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
@@ -532,10 +538,15 @@ df11_decode_kernel(KParams p) {
     // complete on both of its entries, and needs no wait that would also
     // drain the previous unit's stores (vmcnt counts loads and stores in
     // issue order).
-    asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1), "v"(cur.pos), "v"(cur.c));
+    asm volatile("" ::"v"(cur.w0), "v"(cur.w1), "v"(cur.w2), "v"(cur.g0), "v"(cur.g1), "v"(cur.pos), "v"(cur.c),
+                 "v"(cur.ue));
     while (true) {
         // the next unit's inputs (a repeat of the last unit at the end, so the
         // loads are unconditional)
+        // Values derived from the lane index are computed again for every
+        // unit rather than held in registers through it: that leaves phase 2
+        // enough registers for eight waves per SIMD without spills.
+        asm volatile("" : "+v"(lane));
         uint64_t un = uniform_u64(u + stride);
         UnitInputs nxt;
         load_unit<kCounts>(p, un < last ? un : last, lane, nxt);
@@ -597,7 +608,7 @@ df11_status check_block(const df11_device_block *b, const uint16_t *out, uint64_
         return DF11_E_INVALID_ARG;
     if (cap < b->n_total) return DF11_E_BUFFER_TOO_SMALL;
     if (!aligned(out, 16) || !aligned(b->stream, 16) || !aligned(b->sign_mant, 16) ||
-        !aligned(b->unit_pos, 8) || !aligned(b->tables, 16))
+        !aligned(b->unit_pos, 8) || !aligned(b->tables, 16) || !aligned(b->unit_end, 2))
         return DF11_E_INVALID_ARG;
     const uint64_t nw = (b->total_bits + 63) / 64, nu = (nw + 63) / 64;
     if (b->n_windows != nw || b->n_units != nu) return DF11_E_INVALID_ARG;
@@ -685,6 +696,7 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     p.gaps = blk->gaps;
     p.unit_pos = blk->unit_pos;
     p.counts = blk->counts;
+    p.unit_end = blk->unit_end;
     p.out = out_bf16;
     p.n_total = blk->n_total;
     p.total_bits = blk->total_bits;

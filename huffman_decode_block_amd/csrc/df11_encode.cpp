@@ -224,8 +224,10 @@ extern "C" df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_
 
 extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t n_mats,
                                             uint32_t n_threads, uint32_t flags, df11_encoded **out) {
-    if (!out || (n_mats && !mats) || (flags & ~DF11_ENCODE_WINDOW_COUNTS)) return DF11_E_INVALID_ARG;
+    if (!out || (n_mats && !mats) || (flags & ~(DF11_ENCODE_WINDOW_COUNTS | DF11_ENCODE_ALIGNED_UNITS)))
+        return DF11_E_INVALID_ARG;
     const bool with_counts = (flags & DF11_ENCODE_WINDOW_COUNTS) != 0;
+    const bool aligned = (flags & DF11_ENCODE_ALIGNED_UNITS) != 0;
     *out = nullptr;
     Source src{mats, std::vector<uint64_t>(n_mats + 1, 0)};
     for (uint32_t m = 0; m < n_mats; ++m) {
@@ -260,6 +262,49 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
     uint32_t n_tables = 0;
     if (df11i::build_tables(code_len, nullptr, 0, &n_tables) != DF11_OK) return DF11_E_FORMAT;
 
+    const uint64_t code_bits = total_bits;  // the codewords alone
+
+    // ---- aligned-units layout: where each group of 32 codes starts.  Group
+    // bit counts in parallel, then one pass in order: a group whose last code
+    // would start in a later unit than its first goes to the next unit, the
+    // rest of the current unit being filler.  Chunks of the packing below
+    // then begin on group boundaries at these positions.
+    constexpr uint64_t kGroup = 32, kUnitBits = 4096;
+    std::vector<uint64_t> gstart;  // per group: first bit (aligned layout only)
+    std::vector<uint16_t> uend;    // per unit: end of its codes from its first bit
+    if (aligned && N) {
+        const uint64_t n_groups = (N + kGroup - 1) / kGroup;
+        std::vector<uint32_t> gbits(n_groups), glast(n_groups);  // bits, offset of the last start
+        run_parallel(T, [&](uint32_t t) {
+            for (uint64_t g = n_groups * t / T; g < n_groups * (t + 1) / T; ++g) {
+                uint32_t b = 0, last = 0;
+                src.visit(g * kGroup, std::min(N, (g + 1) * kGroup), [&](uint64_t, uint16_t x) {
+                    last = b;
+                    b += len32[exponent_of(x)];
+                });
+                gbits[g] = b;
+                glast[g] = last;
+            }
+        });
+        gstart.resize(n_groups);
+        std::vector<std::pair<uint64_t, uint64_t>> filler;  // (unit, end of its codes), in order
+        uint64_t pos = 0;
+        for (uint64_t g = 0; g < n_groups; ++g) {
+            const uint64_t u = pos / kUnitBits;
+            if (pos + glast[g] >= (u + 1) * kUnitBits) {
+                filler.emplace_back(u, pos);
+                pos = (u + 1) * kUnitBits;
+            }
+            gstart[g] = pos;
+            pos += gbits[g];
+        }
+        total_bits = pos;
+        const uint64_t nu = ((total_bits + 63) / 64 + 63) / 64;
+        uend.assign(nu, static_cast<uint16_t>(kUnitBits));
+        for (const auto &f : filler) uend[f.first] = static_cast<uint16_t>(f.second - f.first * kUnitBits);
+        if (nu) uend[nu - 1] = static_cast<uint16_t>(total_bits - (nu - 1) * kUnitBits);
+    }
+
     // ---- sizes and blob layout (256-byte aligned sections)
     const uint64_t n_windows = (total_bits + 63) / 64;
     const uint64_t n_units = (n_windows + 63) / 64;
@@ -292,6 +337,8 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
     s.off_unit_pos = place(8 * (n_units + 1));
     s.counts_bytes = with_counts ? 64 * n_units : 0;
     s.off_counts = with_counts ? place(s.counts_bytes) : 0;
+    s.unit_end_bytes = aligned ? 2 * n_units : 0;
+    s.off_unit_end = aligned ? place(s.unit_end_bytes) : 0;
     s.blob_bytes = off;
 
     void *mem = nullptr;
@@ -332,24 +379,41 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
 
     // ---- chunked packing: bit offset of each chunk, then each chunk packs its
     // codes; words shared with a neighbouring chunk are merged atomically.
-    const uint64_t n_chunks = N ? std::min<uint64_t>(N, uint64_t{T} * 8) : 0;
+    // Chunk boundaries fall on group boundaries in the aligned layout.
+    const uint64_t n_chunks = N ? std::min<uint64_t>(aligned ? (N + kGroup - 1) / kGroup : N, uint64_t{T} * 8) : 0;
+    auto chunk_begin = [&](uint64_t c) {
+        if (!aligned) return N * c / n_chunks;
+        const uint64_t n_groups = (N + kGroup - 1) / kGroup;
+        return std::min(N, n_groups * c / n_chunks * kGroup);
+    };
     std::vector<uint64_t> chunk_bits(n_chunks + 1, 0);
-    run_parallel(T, [&](uint32_t t) {
-        for (uint64_t c = t; c < n_chunks; c += T) {
-            uint64_t b = 0;
-            src.visit(N * c / n_chunks, N * (c + 1) / n_chunks,
-                      [&](uint64_t, uint16_t x) { b += len32[exponent_of(x)]; });
-            chunk_bits[c + 1] = b;
-        }
-    });
-    for (uint64_t c = 0; c < n_chunks; ++c) chunk_bits[c + 1] += chunk_bits[c];
+    if (aligned) {
+        for (uint64_t c = 0; c < n_chunks; ++c) chunk_bits[c] = gstart[chunk_begin(c) / kGroup];
+    } else {
+        run_parallel(T, [&](uint32_t t) {
+            for (uint64_t c = t; c < n_chunks; c += T) {
+                uint64_t b = 0;
+                src.visit(chunk_begin(c), chunk_begin(c + 1), [&](uint64_t, uint16_t x) { b += len32[exponent_of(x)]; });
+                chunk_bits[c + 1] = b;
+            }
+        });
+        for (uint64_t c = 0; c < n_chunks; ++c) chunk_bits[c + 1] += chunk_bits[c];
+    }
 
     run_parallel(T, [&](uint32_t t) {
         for (uint64_t c = t; c < n_chunks; c += T) {
-            const uint64_t i0 = N * c / n_chunks, i1 = N * (c + 1) / n_chunks;
+            const uint64_t i0 = chunk_begin(c), i1 = chunk_begin(c + 1);
             const uint64_t bit0 = chunk_bits[c];
             uint64_t bit = bit0;
-            uint64_t prev_len = i0 ? len32[exponent_of(src.at(i0 - 1))] : 0;
+            // the previous code's start (for the first-start rules); none for the block's first
+            uint64_t prev_start = 0;
+            if (i0) {
+                const uint64_t lp = len32[exponent_of(src.at(i0 - 1))];
+                prev_start = aligned ? gstart[(i0 - 1) / kGroup] : bit0 - lp;
+                if (aligned)  // the previous group's last code: its start from the group's
+                    src.visit((i0 - 1) / kGroup * kGroup, i0 - 1,
+                              [&](uint64_t, uint16_t x) { prev_start += len32[exponent_of(x)]; });
+            }
             uint64_t acc = 0;
             uint32_t fill = static_cast<uint32_t>(bit0 & 63);
             uint64_t word = bit0 >> 6;
@@ -362,14 +426,21 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
             src.visit(i0, i1, [&](uint64_t i, uint16_t x) {
                 const uint32_t e = exponent_of(x);
                 const uint32_t l = len32[e];
+                if (aligned && i % kGroup == 0 && gstart[i / kGroup] != bit) {  // a filler before this group
+                    if (fill) flush(true);
+                    bit = gstart[i / kGroup];
+                    acc = 0;
+                    fill = static_cast<uint32_t>(bit & 63);
+                    word = bit >> 6;
+                }
                 // first code start in its window / unit?
                 const uint64_t w = bit >> 6;
-                if (i == 0 || ((bit - prev_len) >> 6) < w) {
+                if (i == 0 || (prev_start >> 6) < w) {
                     gap8[w] = static_cast<uint8_t>(bit - 64 * w);
                     if (with_counts) wfirst[w] = i;
                 }
                 const uint64_t u = bit >> 12;
-                if (i == 0 || ((bit - prev_len) >> 12) < u) unit_pos[u] = i;
+                if (i == 0 || (prev_start >> 12) < u) unit_pos[u] = i;
                 sm[i] = static_cast<uint8_t>(((x >> 8) & 0x80u) | (x & 0x7Fu));
                 const uint64_t cw = code[e];
                 if (fill + l < 64) {
@@ -384,8 +455,8 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
                     acc = spill ? (cw << (64 - spill)) : 0;
                     fill = spill;
                 }
+                prev_start = bit;
                 bit += l;
-                prev_len = l;
             });
             if (fill) flush(true);
         }
@@ -397,15 +468,30 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
             words[k] = __builtin_bswap64(words[k]);
     });
 
-    // ---- gaps: the last window may hold no code start
+    // ---- gaps of windows where no code starts: the end of the unit's codes
+    // minus the window's first bit when it comes later (the last window of
+    // the stream, or one that a filler begins in), else 0 (a window of filler)
     for (uint64_t w = 0; w < n_windows; ++w) {
         if (gap8[w] == 0xFF) {
-            const uint64_t g = total_bits - 64 * w;
-            if (w + 1 != n_windows || g > 31) {
+            const uint64_t u = w / 64;
+            const uint64_t end = aligned ? u * kUnitBits + uend[u] : total_bits;
+            if (!aligned && w + 1 != n_windows) {
+                df11_encoded_free(enc);
+                return DF11_E_FORMAT;
+            }
+            const uint64_t g = end > 64 * w ? end - 64 * w : 0;
+            if (g > 31) {
                 df11_encoded_free(enc);
                 return DF11_E_FORMAT;
             }
             gap8[w] = static_cast<uint8_t>(g);
+        } else if (aligned) {  // a start at or after the end of the unit's codes (only in filler: none)
+            const uint64_t u = w / 64;
+            const uint64_t end = u * kUnitBits + uend[u];
+            if (64 * w + gap8[w] >= end && 64 * w < end) {
+                df11_encoded_free(enc);
+                return DF11_E_FORMAT;
+            }
         }
     }
     const uint64_t n_groups = (n_windows + 7) / 8;  // 8 fields = 5 bytes
@@ -435,6 +521,7 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
             next = wfirst[w];
         }
     }
+    if (aligned) std::memcpy(blob + s.off_unit_end, uend.data(), 2 * n_units);
     uint64_t mu = 0;
     for (uint64_t u = 0; u < n_units; ++u) mu = std::max(mu, unit_pos[u + 1] - unit_pos[u]);
     enc->sec.max_unit_count = mu;
@@ -447,7 +534,7 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
         h -= p * std::log2(p);
     }
     enc->sec.exp_entropy_bits = h;
-    enc->sec.mean_code_len_bits = N ? static_cast<double>(total_bits) / static_cast<double>(N) : 0.0;
+    enc->sec.mean_code_len_bits = N ? static_cast<double>(code_bits) / static_cast<double>(N) : 0.0;
     *out = enc;
     return DF11_OK;
 }
@@ -466,6 +553,7 @@ extern "C" df11_status df11_encoded_sections(const df11_encoded *enc, df11_secti
     out->unit_pos = reinterpret_cast<const uint64_t *>(b + out->off_unit_pos);
     out->tables = b + out->off_tables;
     out->counts = out->counts_bytes ? b + out->off_counts : nullptr;
+    out->unit_end = out->unit_end_bytes ? reinterpret_cast<const uint16_t *>(b + out->off_unit_end) : nullptr;
     return DF11_OK;
 }
 

@@ -91,7 +91,7 @@ typedef struct df11_sections {
     uint32_t n_tables;              /* 256-entry decode tables (root first) */
     uint32_t reserved;
     uint64_t n_total;               /* weights in the block */
-    uint64_t total_bits;            /* sum of all codeword lengths */
+    uint64_t total_bits;            /* stream bits: the codewords (and filler, aligned units) */
     uint64_t n_windows;             /* ceil(total_bits / 64) */
     uint64_t n_units;               /* ceil(n_windows / 64) */
     uint64_t max_unit_count;        /* max over u of unit_pos[u+1] - unit_pos[u] */
@@ -120,6 +120,14 @@ typedef struct df11_sections {
     const uint8_t *counts;
     uint64_t counts_bytes;
     uint64_t off_counts;
+    /* Aligned-units layout (blobs encoded with DF11_ENCODE_ALIGNED_UNITS, else
+     * unit_end = NULL, unit_end_bytes = 0): unit_end[u] = where the codes of
+     * unit u end, in bits from the unit's first bit (1..4096); the bits after
+     * it up to the next unit are zero filler.  total_bits then counts the
+     * stream's bits including the filler. */
+    const uint16_t *unit_end;
+    uint64_t unit_end_bytes;
+    uint64_t off_unit_end;
 } df11_sections;
 
 /* Encodes the concatenation of n_mats BF16 matrices with one shared codebook.
@@ -133,13 +141,21 @@ df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_mats, uint3
 
 /* Encoder options (bit flags). */
 #define DF11_ENCODE_WINDOW_COUNTS 1u  /* also store the per-window code counts */
+#define DF11_ENCODE_ALIGNED_UNITS 2u  /* lay codes out so that units start on 32-weight boundaries */
 
-/* df11_encode_block with options.  DF11_ENCODE_WINDOW_COUNTS adds a section
- * that is not part of the pages' format: the number of codes starting in
+/* df11_encode_block with options; neither is part of the pages' format.
+ * DF11_ENCODE_WINDOW_COUNTS adds a section: the number of codes starting in
  * each 64-bit window.  It costs one byte per window (about 1.3 % more bytes
  * per decode at 2.7 bits per exponent) and lets DF11_VARIANT_COUNTS skip the
- * counting pass.  Unknown flags: DF11_E_INVALID_ARG; otherwise as
- * df11_encode_block. */
+ * counting pass.  DF11_ENCODE_ALIGNED_UNITS takes the codes in groups of 32
+ * weights and starts a group at the next unit (4,096 stream bits) when one of
+ * its codes would otherwise start in a later unit than its first, leaving the
+ * rest of the unit as zero filler (about 1 % more stream bits, 0.1 % more
+ * bytes per decode).  Every unit then begins at a weight that is a multiple of
+ * 32, so the decode's writes of neighbouring units meet on 64-byte
+ * boundaries; it adds the unit_end section (2 bytes per unit).  Any decode
+ * variant reads both layouts.  Unknown flags: DF11_E_INVALID_ARG; otherwise
+ * as df11_encode_block. */
 df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t n_mats, uint32_t n_threads,
                                  uint32_t flags, df11_encoded **out);
 
@@ -154,7 +170,9 @@ void df11_encoded_free(df11_encoded *enc);
  * total_bits, unit_pos non-decreasing from 0 to n_total, max_unit_count,
  * decode tables equal to the ones built from code_len, and when present, per
  * window counts of at most 64 that sum over each unit to its unit_pos
- * difference).  It does not decode the stream.  Returns DF11_OK or DF11_E_FORMAT / DF11_E_INVALID_ARG. */
+ * difference; for the aligned-units layout, unit positions that are multiples
+ * of 32, unit ends within their units, zero filler and gaps consistent with
+ * the unit ends).  It does not decode the stream.  Returns DF11_OK or DF11_E_FORMAT / DF11_E_INVALID_ARG. */
 df11_status df11_validate(const df11_sections *s);
 
 /* Decode tables for the GPU kernel, derived from the 256 code lengths: a
@@ -186,6 +204,7 @@ typedef struct df11_device_block {
     uint32_t version;
     uint32_t n_tables;
     const uint8_t *counts;          /* per-window counts, 64 * n_units bytes, or NULL */
+    const uint16_t *unit_end;       /* aligned-units layout: n_units entries, or NULL */
 } df11_device_block;
 
 /* Fills *out for a device copy of a whole blob starting at device_blob. */

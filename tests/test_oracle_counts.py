@@ -114,4 +114,4 @@ def test_unknown_encoder_flags_are_rejected():
     views[0].data = x.ctypes.data
     views[0].numel = x.size
     h = hdb._vp()
-    assert hdb.lib().df11_encode_block_ex(views, 1, 0, 2, hdb.ctypes.byref(h)) == hdb.DF11_E_INVALID_ARG
+    assert hdb.lib().df11_encode_block_ex(views, 1, 0, 4, hdb.ctypes.byref(h)) == hdb.DF11_E_INVALID_ARG
