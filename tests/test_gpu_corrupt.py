@@ -1,7 +1,7 @@
 """GPU: a block whose section contents are corrupted on the device (after the
-host-side checks) decodes to garbage but never writes outside its output
-range, and decode tables that would not advance make the multi-code kernels
-store nothing.  The kernel's own bounds are what is tested: stores go through
+host-side checks), in the pages' format and the aligned-units layout,
+decodes to garbage but never writes outside its output range, and decode
+tables that would not advance make the multi-code kernels store nothing.  The kernel's own bounds are what is tested: stores go through
 buffer ranges clamped to [0, n_total), sub-table indices are clamped, every
 table step advances, and staging writes are bounded by the staging size."""
 import ctypes
@@ -32,6 +32,12 @@ def sections():
     return x, hdb.df11_encode_block([x], window_counts=True).sections
 
 
+@pytest.fixture(scope="module")
+def aligned_sections():
+    x = di.random_normal(200_003, 0.02, 43)
+    return x, hdb.df11_encode_block([x], window_counts=True, aligned_units=True).sections
+
+
 class Block:
     """Device copies of every section, and the df11_device_block over them."""
 
@@ -40,6 +46,8 @@ class Block:
         _, n_tables = hdb.df11_tables_size(s.code_len)
         arrays = {"tables": tables, "stream": s.stream, "sign_mant": s.sign_mant, "gaps": s.gaps,
                   "unit_pos": np.ascontiguousarray(s.unit_pos, dtype=np.uint64), "counts": s.counts}
+        if s.unit_end is not None:
+            arrays["unit_end"] = np.ascontiguousarray(s.unit_end)
         self.t = {}
         for k, a in arrays.items():
             a = np.ascontiguousarray(a).view(np.uint8).reshape(-1)
@@ -53,6 +61,7 @@ class Block:
         b.gaps, b.gaps_bytes = self.t["gaps"].data_ptr(), self.t["gaps"].numel()
         b.unit_pos = self.t["unit_pos"].data_ptr()
         b.counts = self.t["counts"].data_ptr()
+        b.unit_end = self.t["unit_end"].data_ptr() if "unit_end" in self.t else None
         b.n_total, b.total_bits = int(s.n_total), int(s.total_bits)
         b.n_windows, b.n_units = int(s.n_windows), int(s.n_units)
         b.max_unit_count = int(np.diff(s.unit_pos.astype(np.int64)).max())
@@ -94,6 +103,8 @@ def corrupt(torch, blk, case, seed):
     elif case == "unit_pos_reversed":
         v = blk.t["unit_pos"].cpu().numpy().view(np.uint64)[::-1].copy()
         blk.t["unit_pos"].copy_(torch.from_numpy(v.view(np.uint8)))
+    elif case == "unit_end":
+        random_bytes(torch, blk.t["unit_end"], seed)
     elif case == "hier_tables":
         # the hierarchical tables only (the multi-code tables after them stay valid)
         t = blk.t["tables"][: blk.n_hier * 1024]
@@ -113,6 +124,18 @@ def test_corrupt_contents_stay_inside_the_output(torch, sections, case, variant)
     blk = Block(torch, s)
     assert torch.equal(blk.decode(torch, variant)[GUARD:-GUARD].cpu(), torch.from_numpy(x.view(np.int16)))
     corrupt(torch, blk, case, 7)
+    full = blk.decode(torch, variant).cpu().numpy()
+    assert (full[:GUARD] == SENTINEL).all() and (full[-GUARD:] == SENTINEL).all()
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("case", ["unit_end", "stream", "unit_pos_random", "gaps"])
+def test_corrupt_aligned_layout_stays_inside_the_output(torch, aligned_sections, case, variant):
+    x, s = aligned_sections
+    print(f"[gpu-test] corrupt aligned {case}, variant {variant}, n={x.size}", flush=True)
+    blk = Block(torch, s)
+    assert torch.equal(blk.decode(torch, variant)[GUARD:-GUARD].cpu(), torch.from_numpy(x.view(np.int16)))
+    corrupt(torch, blk, case, 9)
     full = blk.decode(torch, variant).cpu().numpy()
     assert (full[:GUARD] == SENTINEL).all() and (full[-GUARD:] == SENTINEL).all()
 
