@@ -19,12 +19,14 @@
 //           are not read again), and their exclusive prefix within each
 //           segment of 256 chunks
 //   top     exclusive prefix of the segment totals (one workgroup)
-//   pack    per chunk: each weight's bit offset (block scan), its
-//           sign/mantissa byte, its code ORed into an LDS bit buffer that is
-//           then written out (global atomic OR only on the two words shared
-//           with the neighbouring chunks), and the first code start of every
-//           window (gap) and unit (position) it contains
+//   pack    persistent, per chunk: each weight's bit offset (block scan),
+//           its sign/mantissa byte, its code and its start ORed into an LDS
+//           bit buffer and an LDS start bitmap; the buffer is written out
+//           (global atomic OR only on the two words shared with the
+//           neighbouring chunks) and the bitmap gives the first code start of
+//           every window (gap) and unit (position) in the chunk
 //   finish  5-bit gap fields (8 windows per 5 bytes) and window counts
+// The aligned-units layout is produced by the host encoder only.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -296,8 +296,9 @@ typedef struct df11_gpu_plan {
 } df11_gpu_plan;
 
 /* Host: the plan for a histogram (host copy of df11_gpu_histogram's result)
- * and encoder flags (DF11_ENCODE_WINDOW_COUNTS or 0).  Errors:
- * DF11_E_INVALID_ARG, DF11_E_FORMAT. */
+ * and encoder flags (DF11_ENCODE_WINDOW_COUNTS or 0; the aligned-units layout
+ * is made by the host encoder only).  Errors: DF11_E_INVALID_ARG (unknown or
+ * unsupported flags), DF11_E_FORMAT. */
 df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t flags, df11_gpu_plan *plan);
 
 /* Encodes x[0..plan->n_total) (device) into the caller's device buffers, sized
