@@ -336,6 +336,8 @@ def main():
                     help="untimed decodes before the warmup steps, for this long (the GPU's clocks ramp up "
                          "over the first ~10 ms of load after host-side work)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cold-launches", type=int, default=20,
+                    help="single launches each after a read of 1 GiB of unrelated data (caches flushed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--overlap", default="",
                     help="comma-separated batch sizes: instead of the main line, measure the decode of block i+1 "
@@ -435,6 +437,21 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     kt = sorted(a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends))
+    # Cold single launches: before each, a read of 1 GiB of unrelated data
+    # pushes the block's sections out of the L2 and the Infinity Cache, leaving
+    # clean lines (not in any interval).
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    cold = []
+    ce = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for i in range(args.cold_launches):
+        flush = scratch.sum()
+        ce[0].record(stream)
+        hdb.df11_decode_block(blk, out=out, stream=stream, launch=launch)
+        ce[1].record(stream)
+        torch.cuda.synchronize()
+        cold.append(ce[0].elapsed_time(ce[1]) * 1e-3)
+    del scratch, flush
+    cold.sort()
     xd = torch.from_numpy(x.view(np.int16)).to(dev)  # and of the last timed decode
     if not torch.equal(out.view(torch.int16), xd):
         raise SystemExit("decode is not bit-exact after timing; refusing to report a number")
@@ -485,7 +502,11 @@ def main():
         "kernel_us": {"avg": round(k_avg * 1e6, 2),
                       "single_launch": {"p10": round(kt[len(kt) // 10] * 1e6, 2),
                                         "p50": round(kt[len(kt) // 2] * 1e6, 2),
-                                        "p90": round(kt[(9 * len(kt)) // 10] * 1e6, 2)}},
+                                        "p90": round(kt[(9 * len(kt)) // 10] * 1e6, 2)},
+                      "cold_single_launch": {"p10": round(cold[len(cold) // 10] * 1e6, 2),
+                                             "p50": round(cold[len(cold) // 2] * 1e6, 2),
+                                             "p90": round(cold[(9 * len(cold)) // 10] * 1e6, 2),
+                                             "launches": len(cold)} if cold else None},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
