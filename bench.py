@@ -439,8 +439,9 @@ def main():
     kt = sorted(a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends))
     # Cold single launches: before each, a read of 1 GiB of unrelated data
     # pushes the block's sections out of the L2 and the Infinity Cache, leaving
-    # clean lines (not in any interval).
-    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    # clean lines (not in any interval).  An int64 sum reads its input as it
+    # is (a narrower type would first be copied, i.e. written, to int64).
+    scratch = torch.ones(1 << 27, dtype=torch.int64, device=dev)
     cold = []
     ce = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     for i in range(args.cold_launches):

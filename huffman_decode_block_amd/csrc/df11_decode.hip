@@ -28,8 +28,9 @@
 //   the next 11 bits (emit table); longer codes fall back to the hierarchical
 //   tables.  A variant reads stored per-window counts instead of phase 1.
 // Staging holds each exponent already shifted into place (exponent << 7) as a
-// 16-bit slot; the multi-code phase 2 ORs whole table entries into zeroed,
-// 8-byte-aligned staging words (unaligned LDS writes stall the LDS pipe).
+// 16-bit slot; the multi-code phase 2 writes a table entry's four slots with
+// four 2-byte LDS stores (one 8-byte store at a 2-byte aligned address would
+// stall the LDS pipe).
 // The merge with the sign/mantissa bytes is one byte permute and one bitfield
 // insert per pair of weights, and the output goes out as 16-byte
 // non-temporal stores (16-bit stores only at the two ends of a unit).
@@ -44,7 +45,7 @@
 namespace {
 
 constexpr uint32_t kLdsTableMax = 32;     // sub-tables beyond this stay in global memory
-constexpr uint32_t kDefaultOversubscribe = 4;
+constexpr uint64_t kUnitsPerWave = 4;     // units each wave walks in the automatic grid (about)
 
 struct KParams {
     const uint32_t *tables;
@@ -209,31 +210,22 @@ struct Look96 {
     }
 };
 
-// Up to four codes per lookup.  The staging is zeroed before phase 2 and
-// every entry is ORed, shifted to the lane's next slot, into the two aligned
-// 8-byte words it covers: aligned LDS accesses are far cheaper than 2-byte
-// aligned ones, and OR needs no order between lanes.  Slots of an entry past
-// its n codes have zero exponent bits, and the control fields sit below the
-// exponent, so the extra bits an entry ORs in never reach an exponent.  An
-// escape entry (first code longer than the index) shifts by 0, ORs nothing
-// but control bits and moves the lane's cursor 64 slots on, which ends the
-// loop with no test in its body; the lane then undoes that, takes the code
-// from the hierarchical tables and goes back in.  Only the lane's last entry
-// may hold codes past its range; it is masked to the codes the lane owns.
-typedef __attribute__((address_space(3))) uint64_t lds_u64;
+// Up to four codes per lookup.  Each step writes the entry's four 16-bit
+// slots at the lane's next slot with four 2-byte LDS stores: the slots past
+// the entry's n codes are rewritten by the lane's next step, so only the
+// lane's own range is ever written and the staging needs no clearing.  The
+// stores are volatile so that they stay 2-byte stores: merged into one
+// 8-byte store at a 2-byte aligned address they would stall the LDS pipe.
+// Slots carry control fields in bits 6..0, below the exponent, which the
+// merge never reads.  An escape entry (first code longer than the index)
+// shifts by 0 and moves the lane's cursor 64 slots on, which ends the loop
+// with no test in its body; the lane then undoes that, takes the code from
+// the hierarchical tables and goes back in (the slots the escape entry wrote
+// lie inside the lane's range and are rewritten).  The last one to three
+// codes are written one slot at a time, only as many as the lane owns.
+typedef __attribute__((address_space(3))) volatile uint16_t lds_u16;
 
-// OR an entry into the staging at LDS byte address b (the lane's next slot):
-// the low part into the aligned word holding b, the slots that do not fit
-// into the next word.  Shift amounts are taken from b << 3, whose low 6 bits
-// (all that a 64-bit shift reads) are 16 x (slot index mod 4).
-__device__ __forceinline__ void stage_or(uint32_t b, uint64_t ev) {
-    lds_u64 *w = reinterpret_cast<lds_u64 *>(b & ~7u);
-    const uint32_t s8 = b << 3;
-    __hip_atomic_fetch_or(w, ev << (s8 & 63u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
-    // ev >> (64 - shift), and nothing for a shift of 0
-    __hip_atomic_fetch_or(w + 1, (ev >> ((48u - s8) & 63u)) >> 16, __ATOMIC_RELAXED,
-                          __HIP_MEMORY_SCOPE_WAVEFRONT);
-}
+__device__ __forceinline__ lds_u16 *lds_slot(uint32_t b) { return reinterpret_cast<lds_u16 *>(b); }
 
 template <bool kDeepGlobal>
 __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et, const KParams &p, Look96 s,
@@ -245,25 +237,31 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
     auto entry = [&]() { return *reinterpret_cast<const uint64_t *>(et + (s.h() >> (32 - df11i::kEmitBits))); };
     auto escape_step = [&]() {
         const uint32_t e = lookup<kDeepGlobal>(lut, p.tables, p.n_tables, s.h());
-        stage_or(b, e >> 16);  // a leaf entry's bits 30..16 are exponent << 7
+        *lds_slot(b) = static_cast<uint16_t>(e >> 16);  // a leaf entry's bits 30..16 are exponent << 7
         b += 2u;
         s.shift(static_cast<uint32_t>(entry_length(e)));
     };
     while (true) {
-        // Each step's ORs are issued after the next step's table read: LDS
-        // operations complete in order, so a wait for the read then leaves
-        // the ORs in flight.  An escape advances b by 64 slots, past bend
-        // (a lane has at most 53 codes left when it meets a code longer
-        // than the index), which ends the loop; it is then undone.
+        // An escape advances b by 64 slots, past bend (a lane has at most 53
+        // codes left when it meets a code longer than the index), which ends
+        // the loop; it is then undone.  Each step's table read is issued
+        // last and waited for at the top of the next step.
         uint64_t ev = entry();
-        asm volatile("" ::"v"(ev));  // wait here, not at the loop head
+        asm volatile("" ::"v"(ev));  // keeps that order (else the read moves to the loop head)
         while (b <= bfull) {
-            const uint32_t lo = static_cast<uint32_t>(ev);
+            const uint32_t lo = static_cast<uint32_t>(ev), hi = static_cast<uint32_t>(ev >> 32);
             s.shift(lo);
-            const uint64_t ev_next = entry();  // past the last step: read, not used
-            stage_or(b, ev);
-            b = __builtin_amdgcn_ubfe(lo, 16u, 7u) * 2u + b;  // n slots, or 64 for an escape
-            ev = ev_next;
+            lds_u16 *w = lds_slot(b);
+            w[0] = static_cast<uint16_t>(lo);
+            w[1] = static_cast<uint16_t>(lo >> 16);
+            w[2] = static_cast<uint16_t>(hi);
+            w[3] = static_cast<uint16_t>(hi >> 16);
+            // n slots, or 64 for an escape; the field is kept opaque so that
+            // the advance is one bitfield extract and one shift-add
+            uint32_t nslots = __builtin_amdgcn_ubfe(lo, 16u, 7u);
+            asm("" : "+v"(nslots));
+            b = nslots * 2u + b;
+            ev = entry();  // past the last step: read, not used
         }
         if (__builtin_expect(b <= bend, 1)) break;
         b -= 2u * df11i::kEmitEscape;
@@ -277,9 +275,12 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
             escape_step();
             continue;
         }
-        const uint32_t left = (bend - b) >> 1;
+        const uint32_t left = (bend - b) >> 1;  // 1..3
         const uint32_t k = m < left ? m : left;
-        stage_or(b, ev & ((uint64_t{1} << (16 * k)) - 1));  // only the lane's own codes
+        lds_u16 *w = lds_slot(b);
+        w[0] = static_cast<uint16_t>(lo);
+        if (k > 1) w[1] = static_cast<uint16_t>(lo >> 16);
+        if (k > 2) w[2] = static_cast<uint16_t>(ev >> 32);
         b += 2u * k;
         s.shift(lo);  // past the lane's last code the state is not used
     }
@@ -386,11 +387,6 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     }
     const uint32_t esm = __builtin_amdgcn_raw_buffer_load_b8(smr, edge ? ek : kOff, 0, 0);
 
-    if constexpr (kMulti) {  // phase 2 ORs into the staging
-        for (uint32_t i = lane; i < p.stage_elems / 8u; i += kChunksPerPass)
-            reinterpret_cast<uint4 *>(stage)[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-
     // ---- this lane's window: gap and end (bits of the stream left in it)
     const uint32_t ulim = p.unit_end ? __builtin_amdgcn_readfirstlane(in.ue)
                                      : u == p.n_units - 1 ? p.last_unit_bits : 4096u;
@@ -423,10 +419,8 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
 
     // ---- phase 2: decode again, stage (exponent << 7) at the output slot
     const uint32_t first = lead + excl;
-    // never past this wave's staging (the multi-code path writes whole
-    // 8-byte words, up to 8 slots past its last one)
-    const uint32_t limit = kMulti ? p.stage_elems - 8u : p.stage_elems;
-    const uint32_t room = first < limit ? limit - first : 0u;
+    // never past this wave's staging (both ways write only the lane's own slots)
+    const uint32_t room = first < p.stage_elems ? p.stage_elems - first : 0u;
     const uint32_t n2 = cnt < room ? cnt : room;
     if constexpr (kMulti)
         emit_multi<kDeepGlobal>(lut, et, p, look, stage, first, n2);
@@ -667,9 +661,8 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     const uint32_t lds_tables = deep_global ? 1u : blk->n_tables;
     const uint32_t fixed_static = multi ? static_cast<uint32_t>(df11i::kMultiTableBytes) : 0u;
     // staging: the unit's outputs after up to 7 slots of lead, rounded to
-    // 8-output chunks, plus one 8-byte word that the multi-code path may OR
-    // past its last slot
-    const uint32_t stage_elems = static_cast<uint32_t>((blk->max_unit_count + 7 + 7) / 8 * 8 + 8);
+    // 8-output chunks
+    const uint32_t stage_elems = static_cast<uint32_t>((blk->max_unit_count + 7 + 7) / 8 * 8);
     // The merge reads whole passes of 64 chunks (up to staged slot 2,047),
     // also past the end of a small unit's staging; the values read there are
     // never stored, and this pad keeps the last wave's such reads inside the
@@ -706,11 +699,17 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
     p.n_tables = blk->n_tables;
     p.stage_elems = stage_elems;
 
-    // Several workgroups per resident slot (each then loops over fewer units)
-    // stream better than one persistent wave of workgroups.
-    const uint32_t over = (launch && launch->oversubscribe) ? launch->oversubscribe : kDefaultOversubscribe;
+    // The automatic grid gives each wave about four units to walk, whatever
+    // the block's size (one persistent wave of workgroups streams worse, and so
+    // do short-lived waves that each pay the table load and the first unit's
+    // latency for one unit), but never fewer workgroups than resident slots.
     const uint64_t groups = (blk->n_units + waves - 1) / waves;
-    uint64_t grid = std::min<uint64_t>(groups, uint64_t(info.cus) * uint64_t(per_cu) * over);
+    const uint64_t resident = uint64_t(info.cus) * uint64_t(per_cu);
+    uint64_t grid;
+    if (launch && launch->oversubscribe)
+        grid = std::min<uint64_t>(groups, resident * launch->oversubscribe);
+    else
+        grid = std::min<uint64_t>(groups, std::max<uint64_t>(resident, (groups + kUnitsPerWave - 1) / kUnitsPerWave));
     if (launch && launch->max_groups) grid = std::min<uint64_t>(grid, launch->max_groups);
     grid = std::max<uint64_t>(grid, 1);
 

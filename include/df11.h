@@ -246,7 +246,9 @@ typedef struct df11_launch {
     uint32_t max_groups;       /* cap on the grid size */
     uint32_t variant;          /* DF11_VARIANT_*, 0 = DF11_VARIANT_MULTI */
     uint32_t oversubscribe;    /* workgroups launched per resident workgroup slot
-                                  (1 = persistent grid); 0 = automatic */
+                                  (1 = persistent grid); 0 = automatic: about
+                                  four units per wave, at least one workgroup
+                                  per resident slot */
 } df11_launch;
 
 /* df11_decode_block with an explicit launch geometry; the output does not
