@@ -81,12 +81,25 @@ __global__ void __launch_bounds__(256) hist_zero(uint64_t *hist) {
 constexpr uint32_t kHistCopies = 16;  // sub-histograms per workgroup, one per lane & 15
 constexpr uint32_t kHistStride = 257; // padded rows: copies of one exponent fall in different banks
 
+// Thread t's 16 weights of chunk c as two 16-byte loads (zeros past the
+// block's end, through a buffer range that stops there).
+__device__ __forceinline__ void hist_load(const uint16_t *x, uint64_t n, uint64_t c, uint32_t t, df11w::v4u &a,
+                                          df11w::v4u &b) {
+    const uint64_t first = c * kChunk;
+    const uint64_t left = first < n ? n - first : 0;
+    const df11w::Rsrc r = df11w::rsrc(x + (first < n ? first : 0), static_cast<uint32_t>(2 * (left < kChunk ? left : kChunk)));
+    a = __builtin_amdgcn_raw_buffer_load_b128(r, 32 * t, 0, 0);
+    b = __builtin_amdgcn_raw_buffer_load_b128(r, 32 * t + 16, 0, 0);
+}
+
 __global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *x, uint64_t n, uint64_t *hist,
                                                         uint16_t *chunk_hist) {
     // A block's values cluster on a few exponents: same-address LDS atomics
     // are serialised, so lanes spread over 16 copies of the histogram.
     // Thread t owns exponent t: after each chunk it adds up and clears the
     // copies of its bin, records the chunk's count and keeps a running total.
+    // Each chunk's weights are requested a chunk ahead; the barriers order LDS
+    // only, so the chunk's count store is not waited for.
     __shared__ uint32_t h[kHistCopies * kHistStride];
     const uint32_t t = threadIdx.x;
     uint32_t *mine = h + (t & (kHistCopies - 1)) * kHistStride;
@@ -94,11 +107,14 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *x, uint6
     __syncthreads();
     const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
     uint64_t total = 0;
-    for (uint64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    uint64_t c = blockIdx.x;
+    df11w::v4u a, b;
+    hist_load(x, n, c, t, a, b);
+    for (; c < n_chunks; c += gridDim.x) {
+        df11w::v4u na, nb;
+        hist_load(x, n, c + gridDim.x, t, na, nb);
         const uint64_t i0 = c * kChunk + uint64_t{t} * kPerThread;
         if (i0 + kPerThread <= n) {
-            const uint4 a = reinterpret_cast<const uint4 *>(x + i0)[0];
-            const uint4 b = reinterpret_cast<const uint4 *>(x + i0)[1];
             const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -108,7 +124,7 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *x, uint6
         } else {
             for (uint64_t i = i0; i < n && i < i0 + kPerThread; ++i) atomicAdd(&mine[exponent_of(x[i])], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         uint32_t cnt = 0;
 #pragma unroll
         for (uint32_t k = 0; k < kHistCopies; ++k) {
@@ -117,7 +133,9 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *x, uint6
         }
         if (chunk_hist) chunk_hist[c * 256 + t] = static_cast<uint16_t>(cnt);  // at most 4,096
         total += cnt;
-        __syncthreads();
+        lds_barrier();
+        a = na;
+        b = nb;
     }
     if (total) atomicAdd(reinterpret_cast<unsigned long long *>(hist + t), static_cast<unsigned long long>(total));
 }
@@ -273,29 +291,26 @@ __device__ __forceinline__ uint32_t clz64(uint64_t v) { return v ? static_cast<u
 
 // What the loop requests for the next chunk while packing the current one.
 // The loaded values are not combined here: any use makes the wave wait.
+// The per-chunk values are the same for every lane but go through vector
+// loads: a scalar load shares its wait counter with the LDS operations, so
+// the chunk's first LDS wait would also wait for the next chunk's values.
 struct ChunkInputs {
-    uint32_t w[4];      // the thread's eight weights, packed
-    uint64_t seg_off;   // the chunk's first bit is seg_off + pre
+    uint32_t w[4];            // the thread's eight weights, packed
+    uint32_t seg_lo, seg_hi;  // the chunk's first bit is seg_off + pre
     uint32_t pre;
-    uint32_t x_last;    // the previous chunk's last weight (chunk 0: not used)
+    uint32_t xw;              // high half: the previous chunk's last weight (chunk 0: not used)
 };
-
-// A load through the scalar data cache (read only): the address is the same
-// for the whole wave, and the wait for it (lgkmcnt) is not ordered with the
-// vector memory stores in flight.
-template <class T>
-__device__ __forceinline__ T scalar_load(const T *ptr) {
-    return *(const __attribute__((address_space(4))) T *)(ptr);
-}
 
 __device__ __forceinline__ void load_inputs(const EncParams &p, uint64_t c, uint32_t t, ChunkInputs &in) {
     const uint64_t cc = c < p.n_chunks ? c : 0;  // past the end: chunk 0 again, not used
-    in.seg_off = scalar_load(p.seg_off + cc / kSegChunks);
-    in.pre = scalar_load(p.chunk_pre + cc);
+    const df11w::v2u so = __builtin_amdgcn_raw_buffer_load_b64(df11w::rsrc(p.seg_off + cc / kSegChunks, 8), 0, 0, 0);
+    in.seg_lo = so.x;
+    in.seg_hi = so.y;
+    in.pre = __builtin_amdgcn_raw_buffer_load_b32(df11w::rsrc(p.chunk_pre + cc, 4), 0, 0, 0);
     // the 4-byte word whose high half is the previous chunk's last weight
     // (chunk 0: any readable word, not used)
     const uint32_t *wl = cc ? reinterpret_cast<const uint32_t *>(p.x + cc * kChunk - 2) : p.chunk_pre;
-    in.x_last = scalar_load(wl) >> 16;
+    in.xw = __builtin_amdgcn_raw_buffer_load_b32(df11w::rsrc(wl, 4), 0, 0, 0);
     load_full(p, c, t, in.w);
 }
 
@@ -311,8 +326,10 @@ __device__ __forceinline__ void pack_chunk(const EncParams &p, uint64_t c, const
     const uint64_t i0 = c * kChunk + uint64_t{t} * kPackPer;
     const uint32_t m = kWhole ? kPackPer : weights_of(p, c, t);
     const uint32_t *wc = in.w;
-    const uint64_t cb = in.seg_off + in.pre;
-    const uint32_t len_last = ent[exponent_of(in.x_last)].y;
+    const uint64_t cb = ((static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(in.seg_hi)) << 32) |
+                         __builtin_amdgcn_readfirstlane(in.seg_lo)) +
+                        __builtin_amdgcn_readfirstlane(in.pre);
+    const uint32_t len_last = ent[exponent_of(in.xw >> 16)].y;
 
     // sign/mantissa bytes, (sign << 7) | mantissa, two weights per word
     uint32_t smw[2];
@@ -360,7 +377,8 @@ __device__ __forceinline__ void pack_chunk(const EncParams &p, uint64_t c, const
         pos += l;
     }
     lds_barrier();
-    asm volatile("" ::"v"(next.w[0]), "v"(next.w[1]), "v"(next.w[2]), "v"(next.w[3]));
+    asm volatile("" ::"v"(next.w[0]), "v"(next.w[1]), "v"(next.w[2]), "v"(next.w[3]), "v"(next.seg_lo),
+                 "v"(next.seg_hi), "v"(next.pre), "v"(next.xw));
 
     // out to HBM as big-endian words, clearing the buffer for the next chunk;
     // the first and last words are shared with the neighbouring chunks when
@@ -371,7 +389,7 @@ __device__ __forceinline__ void pack_chunk(const EncParams &p, uint64_t c, const
     const bool tail_shared = ((cb + chunk_bits) & 31u) != 0;
     uint32_t *out = reinterpret_cast<uint32_t *>(p.stream) + 2 * (cb >> 6);
     const uint64_t room = p.stream_bytes / 4 > 2 * (cb >> 6) ? p.stream_bytes / 4 - 2 * (cb >> 6) : 0;
-    for (uint32_t k = k0 + t; k < nwords; k += blockDim.x) {
+    for (uint32_t k = k0 + t; k < nwords; k += kPackThreads) {
         const uint32_t v = __builtin_bswap32(bits[k]);
         bits[k] = 0;
         if (k >= room) continue;
@@ -435,7 +453,8 @@ __global__ void __launch_bounds__(kPackThreads) pack_kernel(EncParams p) {
     load_inputs(p, c, t, cur);
     // the first chunk's inputs before the loop: its head then sees them
     // complete, with no wait that would also drain the stores
-    asm volatile("" ::"v"(cur.w[0]), "v"(cur.w[1]), "v"(cur.w[2]), "v"(cur.w[3]));
+    asm volatile("" ::"v"(cur.w[0]), "v"(cur.w[1]), "v"(cur.w[2]), "v"(cur.w[3]), "v"(cur.seg_lo),
+                 "v"(cur.seg_hi), "v"(cur.pre), "v"(cur.xw));
     lds_barrier();
 
     while (true) {
