@@ -119,12 +119,15 @@ def copy_context(n_bytes: int, dev, reps: int = 20) -> dict:
     return {"bytes": 2 * half, "copy_us": round(t * 1e6, 2), "copy_GBps": round(2 * half / t / 1e9, 1)}
 
 
-def cpu_baseline(sections, x, min_seconds: float) -> dict:
+def cpu_baseline(sections, x, min_seconds: float, threads: int | None = None) -> dict:
+    """The oracle's unit-parallel bit-serial decode of the whole block, repeated
+    for at least min_seconds, on `threads` host threads (default: the cores this
+    process may use, capped at 16, its share of the machine)."""
     import numpy as np
 
     import oracle
-    # the host cores this process may use, capped at its share of the machine
-    threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS") or 16))
+    if threads is None:
+        threads = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS") or 16))
     enc = oracle.Encoded(n=int(sections.n_total), total_bits=int(sections.total_bits),
                          n_windows=int(sections.n_windows), n_units=int(sections.n_units),
                          code_len=sections.code_len, stream=sections.stream,
@@ -139,10 +142,11 @@ def cpu_baseline(sections, x, min_seconds: float) -> dict:
         if el >= min_seconds:
             break
     ok = bool(np.array_equal(out, x))
+    split = f"units split over {threads} threads" if threads > 1 else "one thread"
     return {"value": round(2.0 * enc.n * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"whole block ({enc.n} weights) decoded {reps}x by the oracle's bit-serial "
-                      f"tree walk, units split over {threads} threads; {el:.1f} s; output == input: {ok}"}
+                      f"tree walk, {split}; {el:.1f} s; output == input: {ok}"}
 
 
 def gpu_encode_bench(args, dev) -> None:
@@ -524,6 +528,7 @@ def main():
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host (cpu_baseline)")
         res["cpu_baseline"] = cpu_baseline(s, x, args.cpu_seconds)
+        res["cpu_baseline_1thread"] = cpu_baseline(s, x, args.cpu_seconds / 3, threads=1)
     print(json.dumps(res), flush=True)
 
 
