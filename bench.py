@@ -119,6 +119,19 @@ def copy_context(n_bytes: int, dev, reps: int = 20) -> dict:
     return {"bytes": 2 * half, "copy_us": round(t * 1e6, 2), "copy_GBps": round(2 * half / t / 1e9, 1)}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(sections, x, min_seconds: float, threads: int | None = None) -> dict:
     """The oracle's unit-parallel bit-serial decode of the whole block, repeated
     for at least min_seconds, on `threads` host threads (default: the cores this
@@ -144,7 +157,7 @@ def cpu_baseline(sections, x, min_seconds: float, threads: int | None = None) ->
     ok = bool(np.array_equal(out, x))
     split = f"units split over {threads} threads" if threads > 1 else "one thread"
     return {"value": round(2.0 * enc.n * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"whole block ({enc.n} weights) decoded {reps}x by the oracle's bit-serial "
                       f"tree walk, {split}; {el:.1f} s; output == input: {ok}"}
 
