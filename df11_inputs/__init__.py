@@ -230,3 +230,59 @@ def many_subtables(r: int = 1000, seed: int = 127) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     rng.shuffle(exps)
     return from_exponents(exps, seed + 1)
+
+
+# ---------------------------------------------------------------- random blocks
+
+RANDOM_FAMILIES = ("normal", "student_t", "any_pattern", "sparse", "skewed", "row_scaled")
+
+
+def random_block(seed: int, max_n: int = 1 << 20, min_n: int = 1) -> tuple:
+    """A seeded random block for property tests: (flat BF16 bits, matrix split,
+    description).  The seed picks a value family (normal with a log-uniform
+    sigma, scaled Student-t, any 16-bit pattern, mostly zeros, a Zipf law over
+    random exponents, or rows with their own scales), a log-uniform size in
+    [min_n, max_n] and a split into 1 to 7 matrices at random points."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([7919, seed])))
+    family = RANDOM_FAMILIES[seed % len(RANDOM_FAMILIES)]
+    n = int(np.exp(rng.uniform(np.log(min_n), np.log(max_n))))
+    sub = int(rng.integers(0, 2**31))
+    if family == "normal":
+        sigma = float(np.exp(rng.uniform(np.log(1e-4), np.log(10.0))))
+        x = random_normal(n, sigma, sub)
+        what = f"normal sigma={sigma:.3g}"
+    elif family == "student_t":
+        df = float(rng.choice([1.0, 2.0, 3.0, 5.0]))
+        scale = float(np.exp(rng.uniform(np.log(1e-3), np.log(1.0))))
+        g = np.random.Generator(np.random.PCG64(sub))
+        x = f32_to_bf16_bits((g.standard_t(df, size=n) * scale).astype(np.float32))
+        what = f"student_t df={df:g} scale={scale:.3g}"
+    elif family == "any_pattern":
+        g = np.random.Generator(np.random.PCG64(sub))
+        x = g.integers(0, 65536, size=n, dtype=np.uint32).astype(np.uint16)
+        what = "any 16-bit pattern"
+    elif family == "sparse":
+        frac = float(rng.uniform(0.5, 0.999))
+        g = np.random.Generator(np.random.PCG64(sub))
+        v = g.standard_normal(n, dtype=np.float32) * np.float32(0.02)
+        v[g.random(n) < frac] = 0.0
+        x = f32_to_bf16_bits(v)
+        what = f"sparse zeros={frac:.3f}"
+    elif family == "skewed":
+        k = int(rng.integers(1, 257))
+        alpha = float(rng.uniform(0.0, 3.0))
+        x = skewed(n, k, alpha, sub)
+        what = f"skewed symbols={k} alpha={alpha:.2f}"
+    else:
+        cols = int(rng.integers(1, 2049))
+        rows = max(1, n // cols)
+        g = np.random.Generator(np.random.PCG64(sub))
+        u = g.uniform(0.5, 2.0, size=rows).astype(np.float32)
+        x = f32_to_bf16_bits((g.standard_normal((rows, cols), dtype=np.float32) *
+                              (np.float32(0.02) * u)[:, None]).reshape(-1))
+        n = x.size
+        what = f"row_scaled {rows}x{cols}"
+    k = int(rng.integers(1, 8))
+    cuts = np.sort(rng.integers(0, n + 1, size=k - 1)) if n else np.zeros(k - 1, dtype=np.int64)
+    mats = np.split(x, cuts)
+    return x, mats, f"{family} n={n} mats={k} ({what})"

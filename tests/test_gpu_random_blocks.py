@@ -1,0 +1,49 @@
+"""GPU parity over seeded random blocks (`df11_inputs.random_block`: six value
+families, log-uniform sizes, splits into 1 to 7 matrices).  Library blobs in
+the pages' format (with window counts) and in the aligned-units layout are
+decoded by every variant, each with a seeded launch geometry, into a buffer
+guarded on both sides, and compared with the input bit for bit (the library's
+sections equal the oracle's on the same blocks: test_random_blocks.py)."""
+import numpy as np
+import pytest
+
+import df11_inputs as di
+import huffman_decode_block_amd as hdb
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 64
+CASES = [(s, 1) for s in range(36)] + [(100 + s, 1 << 20) for s in range(6)]
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "the GPU tests need a GPU"
+    return t
+
+
+def geometry(seed, variant):
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([4241, seed, variant])))
+    waves = int(g.choice([0, 1, 2, 4, 8, 16]))
+    max_groups = int(g.choice([0, 0, 1, 3, 64]))
+    over = int(g.choice([0, 0, 1, 2, 16]))
+    return (waves, max_groups, variant, over)
+
+
+@pytest.mark.parametrize("aligned", [False, True])
+@pytest.mark.parametrize("seed,min_n", CASES)
+def test_random_block_decodes_bit_exactly(torch, seed, min_n, aligned):
+    x, mats, what = di.random_block(seed, max_n=max(min_n, 1 << 20) * 4, min_n=min_n)
+    enc = hdb.df11_encode_block(mats, window_counts=True, aligned_units=aligned)
+    blk = hdb.DeviceBlock.from_encoded(enc)
+    n = x.size
+    for variant in (hdb.DF11_VARIANT_SINGLE, hdb.DF11_VARIANT_MULTI, hdb.DF11_VARIANT_COUNTS):
+        launch = geometry(seed, variant)
+        print(f"[gpu-test] random block {seed}: {what}, aligned={aligned}, launch={launch}", flush=True)
+        buf = torch.full((n + 2 * GUARD,), 0x5A5A, dtype=torch.int16, device="cuda")
+        hdb.df11_decode_block(blk, out=buf[GUARD:GUARD + n], launch=launch)
+        torch.cuda.synchronize()
+        h = buf.cpu().numpy().view(np.uint16)
+        assert (h[:GUARD] == 0x5A5A).all() and (h[GUARD + n:] == 0x5A5A).all(), (what, launch)
+        np.testing.assert_array_equal(h[GUARD:GUARD + n], x, err_msg=f"{what} launch={launch}")
