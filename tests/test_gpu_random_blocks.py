@@ -47,3 +47,21 @@ def test_random_block_decodes_bit_exactly(torch, seed, min_n, aligned):
         h = buf.cpu().numpy().view(np.uint16)
         assert (h[:GUARD] == 0x5A5A).all() and (h[GUARD + n:] == 0x5A5A).all(), (what, launch)
         np.testing.assert_array_equal(h[GUARD:GUARD + n], x, err_msg=f"{what} launch={launch}")
+
+
+@pytest.mark.parametrize("seed,min_n", CASES[::2])
+def test_random_block_gpu_encoding_equals_the_host_encoder(torch, seed, min_n):
+    x, _, what = di.random_block(seed, max_n=max(min_n, 1 << 20) * 4, min_n=min_n)
+    counts = seed % 2 == 0
+    print(f"[gpu-test] gpu encode of random block {seed}: {what}, counts={counts}", flush=True)
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    g = hdb.gpu_encode(xd, window_counts=counts)
+    s = hdb.df11_encode_block([x], window_counts=counts).sections
+    p = g.plan
+    assert bytes(p.code_len) == bytes(s.code_len) and p.total_bits == s.total_bits, what
+    np.testing.assert_array_equal(g.section("stream")[:p.stream_bytes], s.stream, err_msg=what)
+    np.testing.assert_array_equal(g.section("sign_mant")[:p.sign_mant_bytes], s.sign_mant, err_msg=what)
+    np.testing.assert_array_equal(g.section("gaps")[:p.gaps_bytes], s.gaps, err_msg=what)
+    np.testing.assert_array_equal(g.section("unit_pos").view(np.uint64), s.unit_pos, err_msg=what)
+    if counts:
+        np.testing.assert_array_equal(g.section("counts"), s.counts, err_msg=what)
