@@ -21,6 +21,10 @@ extern "C" const char *df11_status_str(df11_status s) {
 
 namespace {
 
+// No block holds more weights (2^48, 512 TB of BF16); below it no size the
+// validator computes from n_total or total_bits can overflow 64 bits.
+constexpr uint64_t kMaxWeights = uint64_t{1} << 48;
+
 uint32_t gap_field(const uint8_t *gaps, uint64_t w) {
     const uint64_t bit = 5 * w;
     const uint32_t two = (uint32_t{gaps[bit >> 3]} << 8) | gaps[(bit >> 3) + 1];
@@ -34,15 +38,17 @@ extern "C" df11_status df11_validate(const df11_sections *s) {
     if (s->version != DF11_FORMAT_VERSION) return DF11_E_UNSUPPORTED;
     if (!s->code_len || !s->stream || !s->gaps || !s->unit_pos || !s->tables) return DF11_E_INVALID_ARG;
     if (s->n_total && !s->sign_mant) return DF11_E_INVALID_ARG;
-    const uint64_t nw = (s->total_bits + 63) / 64, nu = (nw + 63) / 64;
-    if (s->n_windows != nw || s->n_units != nu) return DF11_E_FORMAT;
-    if (s->stream_bytes < 512 * nu + 16 || s->gaps_bytes < 40 * nu + 8 ||
-        s->sign_mant_bytes < (s->n_total + 15) / 16 * 16)
-        return DF11_E_FORMAT;
+    // bounds first, so that no size computed below can wrap around
+    if (s->n_total > kMaxWeights) return DF11_E_FORMAT;
     const bool aligned = s->unit_end_bytes != 0;
     // filler (aligned units) adds at most the rest of a unit to the codes
     if (s->total_bits < s->n_total ||
         s->total_bits > (aligned ? 2u : 1u) * uint64_t{DF11_MAX_CODE_LEN} * s->n_total)
+        return DF11_E_FORMAT;
+    const uint64_t nw = (s->total_bits + 63) / 64, nu = (nw + 63) / 64;
+    if (s->n_windows != nw || s->n_units != nu) return DF11_E_FORMAT;
+    if (s->stream_bytes < 512 * nu + 16 || s->gaps_bytes < 40 * nu + 8 ||
+        s->sign_mant_bytes < (s->n_total + 15) / 16 * 16)
         return DF11_E_FORMAT;
     // code lengths: a prefix code of at most 32 bits; tables match them
     uint32_t code[256];

@@ -46,6 +46,7 @@ namespace {
 
 constexpr uint32_t kLdsTableMax = 32;     // sub-tables beyond this stay in global memory
 constexpr uint64_t kUnitsPerWave = 4;     // units each wave walks in the automatic grid (about)
+constexpr uint64_t kMaxWeights = uint64_t{1} << 48;  // no block holds more (512 TB of BF16)
 
 struct KParams {
     const uint32_t *tables;
@@ -601,6 +602,11 @@ df11_status check_block(const df11_device_block *b, const uint16_t *out, uint64_
     if (!out || !b->tables || !b->stream || !b->sign_mant || !b->gaps || !b->unit_pos)
         return DF11_E_INVALID_ARG;
     if (cap < b->n_total) return DF11_E_BUFFER_TOO_SMALL;
+    // bounds first, so that no size computed below can wrap around: each code
+    // takes 1..32 bits (up to twice that with the aligned layout's filler)
+    if (b->n_total > kMaxWeights || b->total_bits < b->n_total ||
+        b->total_bits > (b->unit_end ? 2u : 1u) * uint64_t{DF11_MAX_CODE_LEN} * b->n_total)
+        return DF11_E_INVALID_ARG;
     if (!aligned(out, 16) || !aligned(b->stream, 16) || !aligned(b->sign_mant, 16) ||
         !aligned(b->unit_pos, 8) || !aligned(b->tables, 16) || !aligned(b->unit_end, 2))
         return DF11_E_INVALID_ARG;

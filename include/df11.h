@@ -172,7 +172,12 @@ void df11_encoded_free(df11_encoded *enc);
  * window counts of at most 64 that sum over each unit to its unit_pos
  * difference; for the aligned-units layout, unit positions that are multiples
  * of 32, unit ends within their units, zero filler and gaps consistent with
- * the unit ends).  It does not decode the stream.  Returns DF11_OK or DF11_E_FORMAT / DF11_E_INVALID_ARG. */
+ * the unit ends).  It does not decode the stream.  The arrays must hold what
+ * the fields say: stream_bytes, sign_mant_bytes, gaps_bytes, counts_bytes and
+ * unit_end_bytes bytes, n_units + 1 unit positions, tables_bytes of tables;
+ * n_total and total_bits are bounded (at most 2^48 weights, at most 32 bits
+ * per weight, 64 with filler) before any size is derived from them.  Returns
+ * DF11_OK or DF11_E_FORMAT / DF11_E_INVALID_ARG. */
 df11_status df11_validate(const df11_sections *s);
 
 /* Decode tables for the GPU kernel, derived from the 256 code lengths: a
@@ -217,7 +222,9 @@ df11_status df11_device_block_from_blob(const df11_sections *s, const void *devi
  * synchronize and allocates nothing.  Exactly n_total elements are written;
  * nothing else is touched.  Argument, capacity, alignment and version errors
  * are reported synchronously (DF11_E_INVALID_ARG, DF11_E_BUFFER_TOO_SMALL,
- * DF11_E_UNSUPPORTED); a launch failure returns DF11_E_HIP.  Corrupted
+ * DF11_E_UNSUPPORTED); so are sizes that no encoder produces (more than 2^48
+ * weights, fewer than 1 or more than 32 bits per weight, 64 with the aligned
+ * layout's filler: DF11_E_INVALID_ARG).  A launch failure returns DF11_E_HIP.  Corrupted
  * section contents are not detected on the device, but every store stays in
  * [0, n_total) and every loop is bounded.  n_total = 0 is a no-op. */
 df11_status df11_decode_block(const df11_device_block *blk, uint16_t *out_bf16,

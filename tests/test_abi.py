@@ -75,6 +75,19 @@ def test_decode_argument_checks_return_before_any_launch():
     bad = hdb.df11_device_block.from_buffer_copy(blk)
     bad.max_unit_count = 5000
     assert L.df11_decode_block(ctypes.byref(bad), 1 << 24, 1000, None) == hdb.DF11_E_INVALID_ARG
+    # sizes that no encoder produces are refused before any size is derived
+    # from them; every other field is made consistent with the bad one, so
+    # that only this check can refuse
+    for n_total, total_bits in ((1000, 33 * 1000), (1000, 999), (1000, (1 << 64) - 1), (1 << 50, 1 << 52)):
+        bad = hdb.df11_device_block.from_buffer_copy(blk)
+        bad.n_total, bad.total_bits = n_total, total_bits
+        nw = ((total_bits + 63) % (1 << 64)) // 64  # wraps like uint64 arithmetic
+        nu = (nw + 63) // 64
+        bad.n_windows, bad.n_units = nw, nu
+        bad.stream_bytes, bad.gaps_bytes = 512 * nu + 16, 40 * nu + 8
+        bad.sign_mant_bytes = (n_total + 15) // 16 * 16
+        got = L.df11_decode_block(ctypes.byref(bad), 1 << 24, n_total, None)
+        assert got == hdb.DF11_E_INVALID_ARG, (n_total, total_bits, got)
     launch = hdb.df11_launch(3, 0)
     assert L.df11_decode_block_ex(ctypes.byref(blk), 1 << 24, 1000, None,
                                   ctypes.byref(launch)) == hdb.DF11_E_INVALID_ARG

@@ -120,7 +120,8 @@ def test_tables_reject_non_prefix_lengths():
 
 
 @pytest.mark.parametrize("what", ["unit_pos_order", "unit_pos_end", "gap_past_end", "code_len",
-                                  "tables", "max_unit_count"])
+                                  "tables", "max_unit_count", "huge_n_total", "huge_total_bits",
+                                  "total_bits_wraps"])
 def test_validate_detects_corruption(what):
     x = di.random_normal(300_000, 0.02, 21)
     enc = hdb.df11_encode_block([x])
@@ -143,6 +144,16 @@ def test_validate_detects_corruption(what):
         s.tables[5] ^= 1
     elif what == "max_unit_count":
         s.raw.max_unit_count += 1
+    elif what == "huge_n_total":
+        # sizes derived from these fields would wrap; rejected before any is read
+        s.raw.n_total = 1 << 62
+        s.raw.total_bits = 1 << 63
+    elif what == "huge_total_bits":
+        s.raw.total_bits = 33 * s.n_total
+    elif what == "total_bits_wraps":
+        s.raw.total_bits = (1 << 64) - 1
+        s.raw.n_windows = 0
+        s.raw.n_units = 0
     assert hdb.df11_validate(s) == hdb.DF11_E_FORMAT
 
 
