@@ -39,6 +39,7 @@
 namespace {
 
 constexpr uint32_t kThreads = 256;
+constexpr uint64_t kMaxWeights = uint64_t{1} << 48;  // no block holds more (512 TB of BF16)
 constexpr uint32_t kPerThread = 16;                   // weights per thread in hist
 constexpr uint32_t kChunk = kThreads * kPerThread;    // 4,096 weights per chunk
 constexpr uint32_t kSegChunks = kThreads;             // chunks per segment of the two-level scan
@@ -584,7 +585,12 @@ extern "C" df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t fl
     if (!hist || !plan || (flags & ~DF11_ENCODE_WINDOW_COUNTS)) return DF11_E_INVALID_ARG;
     df11_gpu_plan q{};
     uint64_t n = 0;
-    for (int e = 0; e < 256; ++e) n += hist[e];
+    for (int e = 0; e < 256; ++e) {
+        // a histogram of more weights than any block holds: refused before the
+        // sums below can wrap around
+        if (hist[e] > kMaxWeights || n + hist[e] > kMaxWeights) return DF11_E_INVALID_ARG;
+        n += hist[e];
+    }
     if (df11i::code_lengths_for(hist, q.code_len, &q.max_code_len, &q.n_symbols, &q.total_bits) != DF11_OK)
         return DF11_E_FORMAT;
     if (df11i::build_tables(q.code_len, nullptr, 0, &q.n_tables) != DF11_OK) return DF11_E_FORMAT;
@@ -609,6 +615,7 @@ extern "C" df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t
     if (!plan || !stream || !sign_mant || !gaps || !unit_pos || !workspace) return DF11_E_INVALID_ARG;
     const bool with_counts = (plan->flags & DF11_ENCODE_WINDOW_COUNTS) != 0;
     if (with_counts != (counts != nullptr) || (plan->n_total && (!x || !chunk_hist))) return DF11_E_INVALID_ARG;
+    if (plan->n_total > kMaxWeights) return DF11_E_INVALID_ARG;  // no size below can then wrap around
     if (!aligned(x, 16) || !aligned(chunk_hist, 16) || !aligned(stream, 16) || !aligned(sign_mant, 16) ||
         !aligned(unit_pos, 8) || !aligned(workspace, 16))
         return DF11_E_INVALID_ARG;

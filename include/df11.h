@@ -307,7 +307,8 @@ typedef struct df11_gpu_plan {
 /* Host: the plan for a histogram (host copy of df11_gpu_histogram's result)
  * and encoder flags (DF11_ENCODE_WINDOW_COUNTS or 0; the aligned-units layout
  * is made by the host encoder only).  Errors: DF11_E_INVALID_ARG (unknown or
- * unsupported flags), DF11_E_FORMAT. */
+ * unsupported flags, or more than 2^48 weights in the histogram),
+ * DF11_E_FORMAT. */
 df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t flags, df11_gpu_plan *plan);
 
 /* Encodes x[0..plan->n_total) (device) into the caller's device buffers, sized
@@ -318,7 +319,9 @@ df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t flags, df11_g
  * the per-chunk counts df11_gpu_histogram took the plan's histogram from.
  * The decode tables are built on the host with
  * df11_build_tables(plan->code_len).  Errors: DF11_E_INVALID_ARG (null or
- * misaligned pointers, flags that do not match), DF11_E_HIP. */
+ * misaligned pointers, flags that do not match, a plan whose sizes do not
+ * follow from n_total and total_bits or that has more than 2^48 weights),
+ * DF11_E_HIP. */
 df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint16_t *chunk_hist,
                             uint8_t *stream, uint8_t *sign_mant, uint8_t *gaps, uint64_t *unit_pos,
                             uint8_t *counts, void *workspace, void *hip_stream);

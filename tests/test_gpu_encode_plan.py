@@ -45,6 +45,33 @@ def test_plan_rejects_bad_arguments():
         hdb.df11_gpu_plan_build(np.zeros(255, np.uint64))
 
 
+def test_plan_refuses_histograms_beyond_any_block():
+    big = np.zeros(256, np.uint64)
+    big[127] = 1 << 49
+    with pytest.raises(hdb.DF11Error):
+        hdb.df11_gpu_plan_build(big)
+    # counts whose sum wraps around 2^64
+    wrap = np.zeros(256, np.uint64)
+    wrap[10] = wrap[11] = np.uint64(1 << 63)
+    with pytest.raises(hdb.DF11Error):
+        hdb.df11_gpu_plan_build(wrap)
+
+
 def test_empty_histogram_gives_an_empty_block():
     plan = hdb.df11_gpu_plan_build(np.zeros(256, np.uint64))
     assert plan.n_total == 0 and plan.total_bits == 0 and plan.n_units == 0
+
+
+def test_encode_refuses_plans_beyond_any_block_before_any_launch():
+    # a plan whose sizes all follow from its n_total and total_bits, but with
+    # more weights than any block holds; the pointers are placeholders that are
+    # never dereferenced (the call returns before any HIP call)
+    import ctypes
+    x = di.random_normal(10_000, 0.02, 3)
+    plan = hdb.df11_gpu_plan_build(oracle.histogram(x).astype(np.uint64))
+    big = hdb.df11_gpu_plan.from_buffer_copy(plan)
+    big.n_total = 1 << 50
+    big.sign_mant_bytes = (big.n_total + 15) // 16 * 16
+    fake = 1 << 20
+    st = hdb.lib().df11_gpu_encode(ctypes.byref(big), fake, fake, fake, fake, fake, fake, None, fake, None)
+    assert st == hdb.DF11_E_INVALID_ARG
