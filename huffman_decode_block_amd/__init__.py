@@ -400,6 +400,22 @@ class DeviceBlock:
         return int(r.stream_bytes + r.sign_mant_bytes + r.gaps_bytes + 8 * (r.n_units + 1) + r.tables_bytes)
 
 
+def _device_tensor(t, name, min_bytes=0, sixteen_bit=False, dev=None):
+    """Checks a tensor handed to the library: on a GPU (the given one, if any),
+    contiguous, of at least min_bytes; raises before anything is launched."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, not {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if sixteen_bit and t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold 16-bit values")
+    if t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {min_bytes} needed")
+
+
 def _stream_handle(stream, device):
     import torch
     if stream is None:
@@ -422,12 +438,13 @@ def df11_decode_block(block: DeviceBlock, out=None, stream=None, launch=None):
     if not out.is_contiguous():
         raise ValueError("out must be contiguous")
     h = _stream_handle(stream, out.device)
-    if launch is None:
-        st = lib().df11_decode_block(ctypes.byref(block.raw), out.data_ptr(), out.numel(), h)
-    else:
-        L = launch if isinstance(launch, df11_launch) else df11_launch(*launch)
-        st = lib().df11_decode_block_ex(ctypes.byref(block.raw), out.data_ptr(), out.numel(), h,
-                                        ctypes.byref(L))
+    with torch.cuda.device(out.device):  # the launch goes to the output's GPU
+        if launch is None:
+            st = lib().df11_decode_block(ctypes.byref(block.raw), out.data_ptr(), out.numel(), h)
+        else:
+            L = launch if isinstance(launch, df11_launch) else df11_launch(*launch)
+            st = lib().df11_decode_block_ex(ctypes.byref(block.raw), out.data_ptr(), out.numel(), h,
+                                            ctypes.byref(L))
     _check(st, "df11_decode_block")
     return out
 
@@ -446,9 +463,17 @@ def df11_gpu_histogram(x, hist, chunk_hist=None, stream=None) -> None:
     """hist (device, 256 int64) := exponent histogram of x (16-bit device
     tensor); chunk_hist (device, df11_gpu_chunk_hist_bytes(x.numel()) bytes, or
     None) := the 256 counts of every chunk of 4,096 weights, as uint16."""
+    import torch
+    _device_tensor(x, "x", sixteen_bit=True)
+    _device_tensor(hist, "hist", 256 * 8, dev=x.device)
+    if hist.element_size() != 8:
+        raise TypeError("hist must hold 64-bit counts")
+    if chunk_hist is not None:
+        _device_tensor(chunk_hist, "chunk_hist", df11_gpu_chunk_hist_bytes(x.numel()), dev=x.device)
     ptr = None if chunk_hist is None else chunk_hist.data_ptr()
-    _check(lib().df11_gpu_histogram(x.data_ptr(), x.numel(), hist.data_ptr(), ptr, _stream_handle(stream, x.device)),
-           "df11_gpu_histogram")
+    with torch.cuda.device(x.device):
+        st = lib().df11_gpu_histogram(x.data_ptr(), x.numel(), hist.data_ptr(), ptr, _stream_handle(stream, x.device))
+    _check(st, "df11_gpu_histogram")
 
 
 def df11_gpu_plan_build(hist, flags: int = 0) -> df11_gpu_plan:
@@ -466,11 +491,21 @@ def df11_gpu_encode(plan: df11_gpu_plan, x, chunk_hist, stream_buf, sign_mant, g
     """Packs the sections of x (device) into the given device tensors (sizes
     from the plan); chunk_hist holds the per-chunk counts df11_gpu_histogram
     took from the same x."""
+    import torch
+    _device_tensor(x, "x", 2 * int(plan.n_total), sixteen_bit=True)
+    need = {"stream_buf": (stream_buf, plan.stream_bytes), "sign_mant": (sign_mant, plan.sign_mant_bytes),
+            "gaps": (gaps, plan.gaps_bytes), "unit_pos": (unit_pos, plan.unit_pos_bytes),
+            "counts": (counts, plan.counts_bytes), "workspace": (workspace, plan.workspace_bytes),
+            "chunk_hist": (chunk_hist, df11_gpu_chunk_hist_bytes(int(plan.n_total)))}
+    for name, (t, nbytes) in need.items():
+        if t is not None:  # a missing section is the library's to refuse
+            _device_tensor(t, name, int(nbytes), dev=x.device)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    _check(lib().df11_gpu_encode(ctypes.byref(plan), ptr(x), ptr(chunk_hist), ptr(stream_buf), ptr(sign_mant),
-                                 ptr(gaps), ptr(unit_pos), ptr(counts), ptr(workspace),
-                                 _stream_handle(stream, x.device)),
-           "df11_gpu_encode")
+    with torch.cuda.device(x.device):
+        st = lib().df11_gpu_encode(ctypes.byref(plan), ptr(x), ptr(chunk_hist), ptr(stream_buf), ptr(sign_mant),
+                                   ptr(gaps), ptr(unit_pos), ptr(counts), ptr(workspace),
+                                   _stream_handle(stream, x.device))
+    _check(st, "df11_gpu_encode")
 
 
 class GpuEncoded:

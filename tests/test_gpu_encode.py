@@ -133,9 +133,24 @@ def test_argument_errors(torch):
     with pytest.raises(hdb.DF11Error) as ei:  # counts given, but the plan has none
         hdb.df11_gpu_encode(plan, xd, ch, *args, buf(64 * plan.n_units), buf(plan.workspace_bytes))
     assert ei.value.status == hdb.DF11_E_INVALID_ARG
-    with pytest.raises(hdb.DF11Error) as ei:  # misaligned input
-        hdb.df11_gpu_encode(plan, xd[1:], ch, *args, None, buf(plan.workspace_bytes))
+    shifted = torch.empty(x.size + 8, dtype=torch.int16, device="cuda")[1:x.size + 1]
+    shifted.copy_(xd)
+    with pytest.raises(hdb.DF11Error) as ei:  # misaligned input (the library refuses it)
+        hdb.df11_gpu_encode(plan, shifted, ch, *args, None, buf(plan.workspace_bytes))
     assert ei.value.status == hdb.DF11_E_INVALID_ARG
+    # tensors smaller than the plan's sections are refused before any launch
+    with pytest.raises(ValueError):
+        hdb.df11_gpu_encode(plan, xd, ch, buf(plan.stream_bytes - 1), *args[1:], None, buf(plan.workspace_bytes))
+    with pytest.raises(ValueError):
+        hdb.df11_gpu_encode(plan, xd[:-1], ch, *args, None, buf(plan.workspace_bytes))
+    with pytest.raises(ValueError):
+        hdb.df11_gpu_encode(plan, xd, ch, *args, None, buf(plan.workspace_bytes - 1))
+    with pytest.raises(ValueError):
+        hdb.df11_gpu_histogram(xd, h, ch[:8])
+    with pytest.raises(TypeError):
+        hdb.df11_gpu_histogram(xd, torch.empty(512, dtype=torch.int32, device="cuda"))
+    with pytest.raises(TypeError):
+        hdb.df11_gpu_histogram(xd.float(), h)
     with pytest.raises(hdb.DF11Error) as ei:  # no per-chunk counts
         hdb.df11_gpu_encode(plan, xd, None, *args, None, buf(plan.workspace_bytes))
     assert ei.value.status == hdb.DF11_E_INVALID_ARG
