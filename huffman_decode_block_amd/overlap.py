@@ -38,7 +38,13 @@ class DecodeAhead:
         self.bufs = [torch.empty(n_max, dtype=torch.bfloat16, device=self.device) for _ in range(2)]
         # default priority: streams of other priorities are not used here
         self.side = side_stream if side_stream is not None else torch.cuda.Stream(self.device)
+        for t in self.bufs:  # the allocator must not reuse them before the side stream is done
+            t.record_stream(self.side)
         self.launch = launch
+        # per buffer: event after its last consumer, kept across run() calls so
+        # that the next call's first decodes wait for the previous call's last
+        # consumers
+        self._released = [None, None]
 
     def run(self, consume: Callable[[int, list], None], stream=None, order: Sequence[int] | None = None):
         """For each block index in `order` (default: all, in order), call
@@ -48,7 +54,9 @@ class DecodeAhead:
         torch = self.torch
         stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         order = list(range(len(self.blocks))) if order is None else list(order)
-        released = [None, None]  # per buffer: event after its last consumer
+        for t in self.bufs:
+            t.record_stream(stream)
+        released = self._released
 
         def decode(k):
             i, b = order[k], k % 2

@@ -55,3 +55,29 @@ def test_decode_ahead_feeds_exact_weights(torch, order):
             y_ref = F.linear(xs[ref.shape[1]], ref)
             # same operands; the GEMM library may pick its algorithm by pointer alignment
             torch.testing.assert_close(y, y_ref, rtol=1e-2, atol=1e-3)
+
+
+def test_consecutive_runs_do_not_overwrite_a_buffer_still_in_use(torch):
+    # the first run's last consumer of each buffer is held back on its stream
+    # (a bounded spin) while the second run starts decoding into the same
+    # buffers: the second run's decodes must wait for it
+    print("[gpu-test] decode-ahead: two runs back to back", flush=True)
+    blocks, originals = _blocks(torch, 3)
+    ahead = DecodeAhead(blocks, [SHAPES] * 3)
+    stream = torch.cuda.current_stream()
+    seen = []
+
+    def slow(i, views):
+        torch.cuda._sleep(20_000_000)  # about 10 ms of GPU time on the consumer stream
+        seen.append((i, [v.clone() for v in views]))
+
+    def quick(i, views):
+        seen.append((i, [v.clone() for v in views]))
+
+    ahead.run(slow, stream=stream, order=[0, 1])
+    ahead.run(quick, stream=stream, order=[2, 2, 1])
+    torch.cuda.synchronize()
+    assert [i for i, _ in seen] == [0, 1, 2, 2, 1]
+    for i, ws in seen:
+        for w, ref in zip(ws, originals[i]):
+            assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), f"block {i} weights differ"
