@@ -27,7 +27,8 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "huffman_decode_block_amd", "csrc", "df11_decode.hip")
 # the headers of this package that the decode kernel's code includes
-KERNEL_HEADERS = [os.path.join(ROOT, "huffman_decode_block_amd", "csrc", h) for h in ("df11_wave.h",)]
+KERNEL_HEADERS = [os.path.join(ROOT, "huffman_decode_block_amd", "csrc", h) for h in ("df11_wave.h", "df11_internal.h")] \
+    + [os.path.join(ROOT, "include", "df11.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "df11_decode_kernel_c3_hbm_counters.json")
 
 

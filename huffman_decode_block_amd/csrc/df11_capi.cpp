@@ -33,7 +33,9 @@ uint32_t gap_field(const uint8_t *gaps, uint64_t w) {
 
 }  // namespace
 
-extern "C" df11_status df11_validate(const df11_sections *s) {
+namespace {
+
+df11_status validate(const df11_sections *s) {
     if (!s) return DF11_E_INVALID_ARG;
     if (s->version != DF11_FORMAT_VERSION) return DF11_E_UNSUPPORTED;
     if (!s->code_len || !s->stream || !s->gaps || !s->unit_pos || !s->tables) return DF11_E_INVALID_ARG;
@@ -114,6 +116,12 @@ extern "C" df11_status df11_validate(const df11_sections *s) {
         }
     }
     return DF11_OK;
+}
+
+}  // namespace
+
+extern "C" df11_status df11_validate(const df11_sections *s) {
+    return df11i::guarded([&] { return validate(s); });
 }
 
 extern "C" df11_status df11_device_block_from_blob(const df11_sections *s, const void *device_blob,

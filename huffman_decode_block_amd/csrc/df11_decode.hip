@@ -628,9 +628,10 @@ extern "C" const char *df11_hip_error_name(int32_t code) {
     return hipGetErrorName(static_cast<hipError_t>(code));
 }
 
-extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf16,
-                                            uint64_t out_capacity, void *hip_stream,
-                                            const df11_launch *launch) {
+namespace {
+
+df11_status decode_block(const df11_device_block *blk, uint16_t *out_bf16, uint64_t out_capacity, void *hip_stream,
+                         const df11_launch *launch) {
     df11_status rc = check_block(blk, out_bf16, out_capacity);
     if (rc != DF11_OK || blk->n_total == 0) return rc;
     const uint32_t variant = (launch && launch->variant) ? launch->variant : DF11_VARIANT_MULTI;
@@ -729,6 +730,14 @@ extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16
         return DF11_E_HIP;
     }
     return DF11_OK;
+}
+
+}  // namespace
+
+extern "C" df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf16,
+                                            uint64_t out_capacity, void *hip_stream,
+                                            const df11_launch *launch) {
+    return df11i::guarded([&] { return decode_block(blk, out_bf16, out_capacity, hip_stream, launch); });
 }
 
 extern "C" df11_status df11_decode_block(const df11_device_block *blk, uint16_t *out_bf16,

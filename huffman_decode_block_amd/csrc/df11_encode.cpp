@@ -18,6 +18,8 @@
 #include <functional>
 #include <sched.h>
 #include <thread>
+#include <exception>
+#include <memory>
 #include <vector>
 
 #include "df11_internal.h"
@@ -26,17 +28,35 @@ namespace {
 
 using df11i::thread_count;
 
-// Runs fn(t) for t in [0, n) on up to n threads.
+// Runs fn(t) for t in [0, n) on up to n threads.  An exception in any of
+// them, or in starting a thread, is rethrown here once every thread that
+// started has been joined: none escapes a thread or leaves one running.
 void run_parallel(uint32_t n, const std::function<void(uint32_t)> &fn) {
     if (n <= 1) {
         if (n == 1) fn(0);
         return;
     }
+    std::vector<std::exception_ptr> err(n);
+    auto body = [&](uint32_t t) {
+        try {
+            fn(t);
+        } catch (...) {
+            err[t] = std::current_exception();
+        }
+    };
     std::vector<std::thread> pool;
     pool.reserve(n - 1);
-    for (uint32_t t = 1; t < n; ++t) pool.emplace_back(fn, t);
-    fn(0);
+    std::exception_ptr start_err;
+    try {
+        for (uint32_t t = 1; t < n; ++t) pool.emplace_back(body, t);
+    } catch (...) {
+        start_err = std::current_exception();
+    }
+    if (!start_err) body(0);
     for (auto &th : pool) th.join();
+    if (start_err) std::rethrow_exception(start_err);
+    for (auto &e : err)
+        if (e) std::rethrow_exception(e);
 }
 
 // The block as one logical array over the caller's matrices.
@@ -222,8 +242,10 @@ extern "C" df11_status df11_encode_block(const df11_bf16_view *mats, uint32_t n_
     return df11_encode_block_ex(mats, n_mats, n_threads, 0u, out);
 }
 
-extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t n_mats,
-                                            uint32_t n_threads, uint32_t flags, df11_encoded **out) {
+namespace {
+
+df11_status encode_block(const df11_bf16_view *mats, uint32_t n_mats, uint32_t n_threads, uint32_t flags,
+                         df11_encoded **out) {
     if (!out || (n_mats && !mats) || (flags & ~(DF11_ENCODE_WINDOW_COUNTS | DF11_ENCODE_ALIGNED_UNITS)))
         return DF11_E_INVALID_ARG;
     const bool with_counts = (flags & DF11_ENCODE_WINDOW_COUNTS) != 0;
@@ -349,6 +371,8 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
         free(mem);
         return DF11_E_NOMEM;
     }
+    // freed on every way out but success, exceptions included
+    std::unique_ptr<df11_encoded, void (*)(df11_encoded *)> owner(enc, &df11_encoded_free);
     std::memset(blob, 0, s.off_stream);  // header, code_len, mat_offset, tables
     std::memcpy(blob, "DF11", 4);
     std::memcpy(blob + s.off_code_len, code_len, 256);
@@ -476,12 +500,10 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
             const uint64_t u = w / 64;
             const uint64_t end = aligned ? u * kUnitBits + uend[u] : total_bits;
             if (!aligned && w + 1 != n_windows) {
-                df11_encoded_free(enc);
                 return DF11_E_FORMAT;
             }
             const uint64_t g = end > 64 * w ? end - 64 * w : 0;
             if (g > 31) {
-                df11_encoded_free(enc);
                 return DF11_E_FORMAT;
             }
             gap8[w] = static_cast<uint8_t>(g);
@@ -489,7 +511,6 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
             const uint64_t u = w / 64;
             const uint64_t end = u * kUnitBits + uend[u];
             if (64 * w + gap8[w] >= end && 64 * w < end) {
-                df11_encoded_free(enc);
                 return DF11_E_FORMAT;
             }
         }
@@ -514,7 +535,6 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
             if (wfirst[w] == kNoStart) continue;  // only the last window may have none
             const uint64_t c = next - wfirst[w];
             if (c > 64) {
-                df11_encoded_free(enc);
                 return DF11_E_FORMAT;
             }
             counts[w] = static_cast<uint8_t>(c);
@@ -535,8 +555,16 @@ extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t
     }
     enc->sec.exp_entropy_bits = h;
     enc->sec.mean_code_len_bits = N ? static_cast<double>(code_bits) / static_cast<double>(N) : 0.0;
-    *out = enc;
+    *out = owner.release();
     return DF11_OK;
+}
+
+}  // namespace
+
+extern "C" df11_status df11_encode_block_ex(const df11_bf16_view *mats, uint32_t n_mats,
+                                            uint32_t n_threads, uint32_t flags, df11_encoded **out) {
+    if (out) *out = nullptr;
+    return df11i::guarded([&] { return encode_block(mats, n_mats, n_threads, flags, out); });
 }
 
 extern "C" df11_status df11_encoded_sections(const df11_encoded *enc, df11_sections *out) {

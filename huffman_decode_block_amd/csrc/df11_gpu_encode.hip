@@ -581,7 +581,9 @@ extern "C" df11_status df11_gpu_histogram(const uint16_t *x, uint64_t n, uint64_
     return DF11_OK;
 }
 
-extern "C" df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t flags, df11_gpu_plan *plan) {
+namespace {
+
+df11_status plan_build(const uint64_t hist[256], uint32_t flags, df11_gpu_plan *plan) {
     if (!hist || !plan || (flags & ~DF11_ENCODE_WINDOW_COUNTS)) return DF11_E_INVALID_ARG;
     df11_gpu_plan q{};
     uint64_t n = 0;
@@ -609,9 +611,9 @@ extern "C" df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t fl
     return DF11_OK;
 }
 
-extern "C" df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint16_t *chunk_hist,
-                                       uint8_t *stream, uint8_t *sign_mant, uint8_t *gaps, uint64_t *unit_pos,
-                                       uint8_t *counts, void *workspace, void *hip_stream) {
+df11_status gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint16_t *chunk_hist, uint8_t *stream,
+                       uint8_t *sign_mant, uint8_t *gaps, uint64_t *unit_pos, uint8_t *counts, void *workspace,
+                       void *hip_stream) {
     if (!plan || !stream || !sign_mant || !gaps || !unit_pos || !workspace) return DF11_E_INVALID_ARG;
     const bool with_counts = (plan->flags & DF11_ENCODE_WINDOW_COUNTS) != 0;
     if (with_counts != (counts != nullptr) || (plan->n_total && (!x || !chunk_hist))) return DF11_E_INVALID_ARG;
@@ -678,4 +680,18 @@ extern "C" df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t
         return DF11_E_HIP;
     }
     return DF11_OK;
+}
+
+}  // namespace
+
+extern "C" df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t flags, df11_gpu_plan *plan) {
+    return df11i::guarded([&] { return plan_build(hist, flags, plan); });
+}
+
+extern "C" df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint16_t *chunk_hist,
+                                       uint8_t *stream, uint8_t *sign_mant, uint8_t *gaps, uint64_t *unit_pos,
+                                       uint8_t *counts, void *workspace, void *hip_stream) {
+    return df11i::guarded([&] {
+        return gpu_encode(plan, x, chunk_hist, stream, sign_mant, gaps, unit_pos, counts, workspace, hip_stream);
+    });
 }

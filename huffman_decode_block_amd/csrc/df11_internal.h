@@ -2,6 +2,7 @@
 #pragma once
 
 #include <cstdint>
+#include <new>
 
 #include "df11.h"
 
@@ -13,6 +14,20 @@
 //   pointer : bit 31 = 1; bits 30..16 = index of the 256-entry sub-table
 //             indexed by the next 8 stream bits; the length fields read as 8.
 namespace df11i {
+
+// Runs the body of a C entry point so that no C++ exception crosses the C
+// ABI: a failed host allocation, or a thread or lock the system could not
+// provide, becomes DF11_E_NOMEM.
+template <class F>
+df11_status guarded(F &&body) noexcept {
+    try {
+        return body();
+    } catch (const std::bad_alloc &) {
+        return DF11_E_NOMEM;
+    } catch (...) {
+        return DF11_E_NOMEM;
+    }
+}
 
 constexpr uint32_t kPointerFlag = 0x80000000u;
 

@@ -146,17 +146,20 @@ df11_status build_tables(const uint8_t code_len[256], uint32_t *dst, uint64_t ds
 extern "C" df11_status df11_tables_size(const uint8_t code_len[256], uint64_t *bytes,
                                         uint32_t *n_tables) {
     if (!code_len || !bytes) return DF11_E_INVALID_ARG;
-    uint32_t nt = 0;
-    df11_status rc = df11i::build_tables(code_len, nullptr, 0, &nt);
-    if (rc != DF11_OK) return rc;
-    *bytes = df11i::tables_bytes_for(nt);
-    if (n_tables) *n_tables = nt;
-    return DF11_OK;
+    return df11i::guarded([&] {
+        uint32_t nt = 0;
+        const df11_status rc = df11i::build_tables(code_len, nullptr, 0, &nt);
+        if (rc != DF11_OK) return rc;
+        *bytes = df11i::tables_bytes_for(nt);
+        if (n_tables) *n_tables = nt;
+        return DF11_OK;
+    });
 }
 
 extern "C" df11_status df11_build_tables(const uint8_t code_len[256], void *dst,
                                          uint64_t dst_bytes) {
     if (!code_len || !dst) return DF11_E_INVALID_ARG;
-    return df11i::build_tables(code_len, static_cast<uint32_t *>(dst),
-                               dst_bytes / sizeof(uint32_t), nullptr);
+    return df11i::guarded([&] {
+        return df11i::build_tables(code_len, static_cast<uint32_t *>(dst), dst_bytes / sizeof(uint32_t), nullptr);
+    });
 }

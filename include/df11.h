@@ -64,7 +64,7 @@ extern "C" {
 typedef int32_t df11_status;
 #define DF11_OK 0
 #define DF11_E_INVALID_ARG (-1)      /* null pointer, bad size or alignment */
-#define DF11_E_NOMEM (-2)            /* host allocation failed */
+#define DF11_E_NOMEM (-2)            /* host allocation failed (memory, threads or a lock) */
 #define DF11_E_FORMAT (-3)           /* sections are inconsistent */
 #define DF11_E_BUFFER_TOO_SMALL (-4) /* caller buffer shorter than needed */
 #define DF11_E_UNSUPPORTED (-5)      /* version or feature not supported */
