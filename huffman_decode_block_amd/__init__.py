@@ -198,16 +198,20 @@ def _as_u16(m) -> np.ndarray:
     return a.reshape(-1)
 
 
-def _np_view(ptr: int, count: int, dtype) -> np.ndarray:
+def _np_view(ptr: int, count: int, dtype, owner=None) -> np.ndarray:
+    """A numpy view of library memory; it keeps `owner` (the object that frees
+    that memory) alive for as long as the view, or any view of it, exists."""
     if count == 0:
         return np.zeros(0, dtype=dtype)
     ctype = np.ctypeslib.as_ctypes_type(dtype)
     arr = (ctype * count).from_address(ptr)
+    arr._owner = owner
     return np.ctypeslib.as_array(arr)
 
 
 class Sections:
-    """Numpy views of one encoded blob (valid while its Encoded lives)."""
+    """Numpy views of one encoded blob.  Every view keeps the blob's Encoded
+    alive; only an explicit Encoded.free() ends them early."""
 
     def __init__(self, owner, s: df11_sections):
         self._owner = owner
@@ -224,18 +228,18 @@ class Sections:
         self.max_unit_count = s.max_unit_count
         self.exp_entropy_bits = s.exp_entropy_bits
         self.mean_code_len_bits = s.mean_code_len_bits
-        self.code_len = _np_view(s.code_len, 256, np.uint8)
-        self.mat_offset = _np_view(s.mat_offset, s.n_mats + 1, np.uint64)
-        self.stream = _np_view(s.stream, s.stream_bytes, np.uint8)
-        self.sign_mant = _np_view(s.sign_mant, s.sign_mant_bytes, np.uint8)
-        self.gaps = _np_view(s.gaps, s.gaps_bytes, np.uint8)
-        self.unit_pos = _np_view(s.unit_pos, s.n_units + 1, np.uint64)
-        self.tables = _np_view(s.tables, s.tables_bytes, np.uint8)
-        self.blob = _np_view(s.blob, s.blob_bytes, np.uint8)
+        self.code_len = _np_view(s.code_len, 256, np.uint8, owner)
+        self.mat_offset = _np_view(s.mat_offset, s.n_mats + 1, np.uint64, owner)
+        self.stream = _np_view(s.stream, s.stream_bytes, np.uint8, owner)
+        self.sign_mant = _np_view(s.sign_mant, s.sign_mant_bytes, np.uint8, owner)
+        self.gaps = _np_view(s.gaps, s.gaps_bytes, np.uint8, owner)
+        self.unit_pos = _np_view(s.unit_pos, s.n_units + 1, np.uint64, owner)
+        self.tables = _np_view(s.tables, s.tables_bytes, np.uint8, owner)
+        self.blob = _np_view(s.blob, s.blob_bytes, np.uint8, owner)
         # optional per-window code counts (64 * n_units bytes), else None
-        self.counts = _np_view(s.counts, s.counts_bytes, np.uint8) if s.counts_bytes else None
+        self.counts = _np_view(s.counts, s.counts_bytes, np.uint8, owner) if s.counts_bytes else None
         # aligned-units layout: where each unit's codes end, from its first bit; else None
-        self.unit_end = _np_view(s.unit_end, s.n_units, np.uint16) if s.unit_end_bytes else None
+        self.unit_end = _np_view(s.unit_end, s.n_units, np.uint16, owner) if s.unit_end_bytes else None
 
     @property
     def compressed_bytes(self) -> int:

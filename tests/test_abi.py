@@ -95,3 +95,14 @@ def test_decode_argument_checks_return_before_any_launch():
     empty = hdb.df11_encode_block([np.zeros(0, np.uint16)])
     eb = hdb.df11_device_block_from_blob(empty.sections, 1 << 20)
     assert L.df11_decode_block(ctypes.byref(eb), None, 0, None) == hdb.DF11_OK
+
+
+def test_section_views_keep_their_blob_alive():
+    import gc
+    x = np.arange(100_000, dtype=np.uint16)
+    stream = hdb.df11_encode_block([x]).sections.stream  # the Encoded is a temporary
+    copy = stream.copy()
+    gc.collect()
+    junk = [np.full(1 << 16, 0xAB, np.uint8) for _ in range(64)]  # reuse freed memory, if any
+    assert np.array_equal(stream, copy)
+    del junk
