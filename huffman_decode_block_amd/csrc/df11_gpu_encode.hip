@@ -327,9 +327,12 @@ __device__ __forceinline__ void pack_chunk(const EncParams &p, uint64_t c, const
     const uint64_t i0 = c * kChunk + uint64_t{t} * kPackPer;
     const uint32_t m = kWhole ? kPackPer : weights_of(p, c, t);
     const uint32_t *wc = in.w;
-    const uint64_t cb = ((static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(in.seg_hi)) << 32) |
-                         __builtin_amdgcn_readfirstlane(in.seg_lo)) +
-                        __builtin_amdgcn_readfirstlane(in.pre);
+    // readfirstlane returns a signed int: each half is taken as uint32_t before
+    // it is widened (a sign-extended low half would corrupt offsets past 2^31 bits)
+    const uint32_t seg_lo = __builtin_amdgcn_readfirstlane(in.seg_lo);
+    const uint32_t seg_hi = __builtin_amdgcn_readfirstlane(in.seg_hi);
+    const uint32_t chunk_pre = __builtin_amdgcn_readfirstlane(in.pre);
+    const uint64_t cb = ((static_cast<uint64_t>(seg_hi) << 32) | seg_lo) + chunk_pre;
     const uint32_t len_last = ent[exponent_of(in.xw >> 16)].y;
 
     // sign/mantissa bytes, (sign << 7) | mantissa, two weights per word

@@ -113,6 +113,28 @@ def test_workload_c3_full(torch):
     assert g.plan.n_total == x.size
 
 
+def test_round_trip_with_several_segments_per_scan_thread(torch):
+    # 1.2 G weights: more than 1,024 segments of 256 chunks, so each thread of
+    # the one-workgroup offset scan sums several segments.  Generated, encoded
+    # and decoded on the device (seeded); the decode is checked against the
+    # oracle elsewhere, and every section enters it: a wrong offset, gap,
+    # position or count would change the output.
+    n = 1_200_000_003
+    say(f"gpu encode round trip: n={n}")
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    x = (torch.randn(n, device="cuda", generator=gen) * 0.02).to(torch.bfloat16).view(torch.int16)
+    g = hdb.gpu_encode(x, window_counts=True)
+    assert (g.plan.n_total + 4095) // 4096 > 1024 * 256
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    for v in (hdb.DF11_VARIANT_MULTI, hdb.DF11_VARIANT_COUNTS):
+        out.fill_(0x5A5A)
+        hdb.df11_decode_block(g.block, out=out, launch=(0, 0, v))
+        torch.cuda.synchronize()
+        assert torch.equal(out, x), f"variant {v}: decode of the GPU encoding differs"
+    del out, g, x
+    torch.cuda.empty_cache()
+
+
 def test_argument_errors(torch):
     x = di.random_normal(10_000, 0.02, 3)
     xd = torch.from_numpy(x.view(np.int16)).to("cuda")
