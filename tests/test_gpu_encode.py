@@ -113,18 +113,19 @@ def test_workload_c3_full(torch):
     assert g.plan.n_total == x.size
 
 
-def test_round_trip_with_several_segments_per_scan_thread(torch):
-    # 1.2 G weights: more than 1,024 segments of 256 chunks, so each thread of
-    # the one-workgroup offset scan sums several segments.  Generated, encoded
-    # and decoded on the device (seeded); the decode is checked against the
-    # oracle elsewhere, and every section enters it: a wrong offset, gap,
-    # position or count would change the output.
-    n = 1_200_000_003
+def test_round_trip_past_32_bit_sizes(torch):
+    # 2.2 G weights (more than 2^31) and about 5.7 G stream bits (more than
+    # 2^32), in more than 1,024 segments of 256 chunks, so each thread of the
+    # one-workgroup offset scan sums several segments.  Generated, encoded and
+    # decoded on the device (seeded); the decode is checked against the oracle
+    # elsewhere, and every section enters it: a wrong offset, gap, position or
+    # count would change the output.
+    n = 2_200_000_001
     say(f"gpu encode round trip: n={n}")
     gen = torch.Generator(device="cuda").manual_seed(12)
     x = (torch.randn(n, device="cuda", generator=gen) * 0.02).to(torch.bfloat16).view(torch.int16)
     g = hdb.gpu_encode(x, window_counts=True)
-    assert (g.plan.n_total + 4095) // 4096 > 1024 * 256
+    assert (g.plan.n_total + 4095) // 4096 > 1024 * 256 and g.plan.total_bits > 1 << 32 and n > 1 << 31
     out = torch.empty(n, dtype=torch.int16, device="cuda")
     for v in (hdb.DF11_VARIANT_MULTI, hdb.DF11_VARIANT_COUNTS):
         out.fill_(0x5A5A)
