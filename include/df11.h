@@ -111,7 +111,7 @@ typedef struct df11_sections {
     uint64_t off_code_len, off_mat_offset, off_stream, off_sign_mant, off_gaps, off_unit_pos,
         off_tables;
     double exp_entropy_bits;        /* Shannon entropy of the exponents, bits/weight */
-    double mean_code_len_bits;      /* total_bits / n_total */
+    double mean_code_len_bits;      /* codeword bits / n_total (filler excluded) */
     /* Optional per-window code counts (blobs encoded with
      * DF11_ENCODE_WINDOW_COUNTS, else counts = NULL, counts_bytes = 0): byte w
      * is the number of codes that start in window w, i.e. in bits
@@ -177,7 +177,8 @@ void df11_encoded_free(df11_encoded *enc);
  * unit_end_bytes bytes, n_units + 1 unit positions, tables_bytes of tables;
  * n_total and total_bits are bounded (at most 2^48 weights, at most 32 bits
  * per weight, 64 with filler) before any size is derived from them.  Returns
- * DF11_OK or DF11_E_FORMAT / DF11_E_INVALID_ARG. */
+ * DF11_OK or DF11_E_FORMAT / DF11_E_INVALID_ARG (DF11_E_NOMEM if host memory
+ * runs out). */
 df11_status df11_validate(const df11_sections *s);
 
 /* Decode tables for the GPU kernel, derived from the 256 code lengths: a
@@ -188,7 +189,8 @@ df11_status df11_validate(const df11_sections *s);
  * reports the bytes needed and the number of hierarchical tables;
  * df11_build_tables writes them to dst (host memory, dst_bytes at least that
  * size).  Errors: DF11_E_INVALID_ARG, DF11_E_FORMAT (lengths do
- * not form a prefix code of at most 32 bits), DF11_E_BUFFER_TOO_SMALL. */
+ * not form a prefix code of at most 32 bits), DF11_E_BUFFER_TOO_SMALL,
+ * DF11_E_NOMEM. */
 df11_status df11_tables_size(const uint8_t code_len[256], uint64_t *bytes, uint32_t *n_tables);
 df11_status df11_build_tables(const uint8_t code_len[256], void *dst, uint64_t dst_bytes);
 
