@@ -483,8 +483,8 @@ def main():
     # the committed counters were taken on the default (multi-code) kernel
     traffic = measured_traffic(args.workload) if args.variant in (0, 2) and not args.aligned_units else None
     if traffic is None:
-        progress("roofline.traffic is null: the committed HBM counters (profiles/) were taken on the default "
-                 "variant of workload C3 with another kernel code, or on another workload or variant")
+        progress("roofline.traffic is null: no committed HBM counter summary matches this kernel code, "
+                 "workload and variant")
     cc = copy_context(ab["total"], dev)
     cc["decode_over_copy"] = round(achieved / cc["copy_GBps"], 3)
     res = {
