@@ -65,3 +65,30 @@ def test_random_block_gpu_encoding_equals_the_host_encoder(torch, seed, min_n):
     np.testing.assert_array_equal(g.section("unit_pos").view(np.uint64), s.unit_pos, err_msg=what)
     if counts:
         np.testing.assert_array_equal(g.section("counts"), s.counts, err_msg=what)
+
+
+def _decodes_exactly(torch, x, blk, launch):
+    n = x.size
+    buf = torch.full((n + 2 * GUARD,), 0x5A5A, dtype=torch.int16, device="cuda")
+    hdb.df11_decode_block(blk, out=buf[GUARD:GUARD + n], launch=launch)
+    torch.cuda.synchronize()
+    h = buf.cpu().numpy().view(np.uint16)
+    return (h[:GUARD] == 0x5A5A).all() and (h[GUARD + n:] == 0x5A5A).all() and np.array_equal(h[GUARD:GUARD + n], x)
+
+
+@pytest.mark.parametrize("first,last,min_n,max_n", [(1000, 1500, 1, 1 << 22), (2000, 2100, 1 << 20, 1 << 24)])
+def test_wide_sweep(torch, first, last, min_n, max_n):
+    # many more seeds than the cases above, checked in one test each: every
+    # decode variant with its seeded launch geometry, both layouts
+    bad = []
+    for seed in range(first, last):
+        x, mats, what = di.random_block(seed, max_n=max_n, min_n=min_n)
+        for aligned in (False, True):
+            blk = hdb.DeviceBlock.from_encoded(hdb.df11_encode_block(mats, window_counts=True, aligned_units=aligned))
+            for variant in (hdb.DF11_VARIANT_SINGLE, hdb.DF11_VARIANT_MULTI, hdb.DF11_VARIANT_COUNTS):
+                launch = geometry(seed, variant)
+                if not _decodes_exactly(torch, x, blk, launch):
+                    bad.append((seed, what, aligned, launch))
+        if seed % 50 == 0:
+            print(f"[gpu-test] wide sweep: seed {seed}, {len(bad)} mismatches so far", flush=True)
+    assert not bad, bad[:5]
