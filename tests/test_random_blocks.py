@@ -46,3 +46,27 @@ def test_aligned_units_equal_the_oracle(seed):
     np.testing.assert_array_equal(s.sign_mant, o.sign_mant, err_msg=what)
     np.testing.assert_array_equal(oracle.decode_units(o), x, err_msg=what)
     assert hdb.df11_validate(s) == hdb.DF11_OK, what
+
+
+def test_wide_sweep_pages_format():
+    # many more seeds, checked in one test: every section against the oracle
+    for seed in range(3000, 3300):
+        x, mats, what = di.random_block(seed, max_n=1 << 18)
+        o = oracle.encode(x)
+        s = hdb.df11_encode_block(mats, n_threads=1 + seed % 4, window_counts=True).sections
+        assert s.total_bits == o.total_bits, what
+        for a, b in ((s.code_len, o.code_len), (s.stream, o.stream), (s.sign_mant, o.sign_mant), (s.gaps, o.gaps),
+                     (s.unit_pos, o.unit_pos)):
+            assert np.array_equal(a, b), (seed, what)
+        assert np.array_equal(s.counts[:o.n_windows], oracle.window_counts(o)), (seed, what)
+
+
+def test_wide_sweep_aligned_units():
+    for seed in range(4000, 4100):
+        x, mats, what = di.random_block(seed, max_n=1 << 16)
+        o = oracle.encode_aligned_units(x)
+        s = hdb.df11_encode_block(mats, aligned_units=True).sections
+        assert s.total_bits == o.total_bits, what
+        for a, b in ((s.stream, o.stream), (s.gaps, o.gaps), (s.unit_pos, o.unit_pos), (s.unit_end, o.unit_end),
+                     (s.sign_mant, o.sign_mant)):
+            assert np.array_equal(a, b), (seed, what)
