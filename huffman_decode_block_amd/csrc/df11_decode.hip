@@ -487,48 +487,74 @@ df11_decode_kernel(KParams p) {
     // dynamic LDS: hierarchical tables, then one staging area per wave
     const uint32_t lds_tables = kDeepGlobal ? 1u : p.n_tables;
     uint32_t *lut = reinterpret_cast<uint32_t *>(lds);
-    {
-        const uint4 *src = reinterpret_cast<const uint4 *>(p.tables);
-        uint4 *dst = reinterpret_cast<uint4 *>(lut);
-        for (uint32_t i = threadIdx.x; i < lds_tables * 64u; i += blockDim.x) dst[i] = src[i];
-        if constexpr (kMulti) {
-            const uint4 *msrc = reinterpret_cast<const uint4 *>(p.tables + p.n_tables * 256u);
-            uint4 *cdst = reinterpret_cast<uint4 *>(s_count_table);
-            for (uint32_t i = threadIdx.x; i < df11i::kCountEntries / 4u; i += blockDim.x) cdst[i] = msrc[i];
-            msrc += df11i::kCountEntries / 4u;
-            uint4 *edst = reinterpret_cast<uint4 *>(s_emit_table);
-            for (uint32_t i = threadIdx.x; i < df11i::kEmitEntries / 2u; i += blockDim.x) edst[i] = msrc[i];
-        }
-    }
-    __syncthreads();
-    if constexpr (kMulti) {
-        // Every count entry advances (1..10 bits) or is the escape, every emit
-        // entry takes 1..4 codes or is the escape: the loops over them then end
-        // whatever the stream holds.  Tables that break this store nothing.
-        bool bad = false;
-        for (uint32_t i = threadIdx.x; i < df11i::kCountEntries; i += blockDim.x) {
-            const uint32_t t = s_count_table[i] & 0xFFu;
-            bad |= !((t >= 1u && t <= df11i::kCountBits) || s_count_table[i] == df11i::kCountEscape);
-        }
-        for (uint32_t i = threadIdx.x; i < df11i::kEmitEntries; i += blockDim.x) {
-            const uint32_t m = (s_emit_table[i].x >> 16) & 127u;
-            bad |= !((m >= 1u && m <= df11i::kEmitCodes) || m == df11i::kEmitEscape);
-        }
-        if (__syncthreads_or(bad)) return;
-    }
 
     uint32_t lane = threadIdx.x & 63u;
     // wave index and wave count are uniform: keep unit indices in scalar registers
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+    uint64_t u = uniform_u64(uint64_t{blockIdx.x} * waves + wave);
+    const uint64_t last = p.n_units - 1;  // the host launches only for blocks with weights
+    // The first unit's inputs are requested before the tables are copied, so
+    // that the two memory latencies overlap (a wave with no unit loads the
+    // last one and leaves after the workgroup barrier).
+    UnitInputs cur;
+    load_unit<kCounts>(p, u < last ? u : last, lane, cur);
+    // The tables go to LDS in one pass: every thread requests its 16-byte
+    // pieces (up to two per round) before it stores any, so their latencies
+    // overlap.  The multi-code tables are checked in registers on the way:
+    // every count entry advances (1..10 bits) or is the escape, every emit
+    // entry takes 1..4 codes or is the escape, so the loops over them end
+    // whatever the stream holds.  Tables that break this store nothing.
+    {
+        const uint32_t n_hier = lds_tables * 64u;  // 16-byte pieces
+        constexpr uint32_t kCountPieces = df11i::kCountEntries / 4u, kEmitPieces = df11i::kEmitEntries / 2u;
+        const uint32_t n_all = n_hier + (kMulti ? kCountPieces + kEmitPieces : 0u);
+        const uint4 *hsrc = reinterpret_cast<const uint4 *>(p.tables);
+        const uint4 *msrc = reinterpret_cast<const uint4 *>(p.tables + p.n_tables * 256u);
+        bool bad = false;
+        for (uint32_t i0 = threadIdx.x; i0 < n_all; i0 += 2u * blockDim.x) {
+            uint4 v[2];
+#pragma unroll
+            for (uint32_t k = 0; k < 2; ++k) {
+                const uint32_t i = i0 + k * blockDim.x;
+                if (i < n_all) v[k] = i < n_hier ? hsrc[i] : msrc[i - n_hier];
+            }
+#pragma unroll
+            for (uint32_t k = 0; k < 2; ++k) {
+                const uint32_t i = i0 + k * blockDim.x;
+                if (i >= n_all) continue;
+                if (i < n_hier) {
+                    reinterpret_cast<uint4 *>(lut)[i] = v[k];
+                } else if constexpr (kMulti) {
+                    const uint32_t j = i - n_hier;
+                    if (j < kCountPieces) {
+                        reinterpret_cast<uint4 *>(s_count_table)[j] = v[k];
+                        const uint32_t ce[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+                        for (const uint32_t e : ce) {
+                            const uint32_t t = e & 0xFFu;
+                            bad |= !((t >= 1u && t <= df11i::kCountBits) || e == df11i::kCountEscape);
+                        }
+                    } else {
+                        reinterpret_cast<uint4 *>(s_emit_table)[j - kCountPieces] = v[k];
+                        const uint32_t el[2] = {v[k].x, v[k].z};  // low words of the two entries
+                        for (const uint32_t lo : el) {
+                            const uint32_t m = (lo >> 16) & 127u;
+                            bad |= !((m >= 1u && m <= df11i::kEmitCodes) || m == df11i::kEmitEscape);
+                        }
+                    }
+                }
+            }
+        }
+        if constexpr (kMulti) {
+            if (__syncthreads_or(bad)) return;
+        } else {
+            __syncthreads();
+        }
+    }
+
     uint16_t *stage = reinterpret_cast<uint16_t *>(lds + lds_tables * 1024u) + wave * p.stage_elems;
     const uint64_t stride = uniform_u64(uint64_t{gridDim.x} * waves);
-
-    uint64_t u = uniform_u64(uint64_t{blockIdx.x} * waves + wave);
     if (u >= p.n_units) return;  // uniform across the wave
-    const uint64_t last = p.n_units - 1;
-    UnitInputs cur;
-    load_unit<kCounts>(p, u, lane, cur);
     // Wait for the first unit's inputs here: the loop head then sees them
     // complete on both of its entries, and needs no wait that would also
     // drain the previous unit's stores (vmcnt counts loads and stores in
