@@ -541,7 +541,7 @@ df11_status encode_block(const df11_bf16_view *mats, uint32_t n_mats, uint32_t n
             next = wfirst[w];
         }
     }
-    if (aligned) std::memcpy(blob + s.off_unit_end, uend.data(), 2 * n_units);
+    if (aligned && n_units) std::memcpy(blob + s.off_unit_end, uend.data(), 2 * n_units);
     uint64_t mu = 0;
     for (uint64_t u = 0; u < n_units; ++u) mu = std::max(mu, unit_pos[u + 1] - unit_pos[u]);
     enc->sec.max_unit_count = mu;
