@@ -362,16 +362,22 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     const uint32_t chunks = (span + 7) / 8;
     const Rsrc smr = rsrc(p.sm + base, 8 * chunks);
 
-    // Chunks [full_lo, full_hi) lie inside the unit and go out as 16-byte
-    // stores; the at most two partial chunks (the first when the unit starts
-    // inside it, the last when the unit ends inside it) go out element by
-    // element from lanes 0..7 (first chunk) and 8..15 (last chunk).
-    const uint32_t full_lo = lead ? 1u : 0u;
-    const uint32_t full_hi = span / 8;
-    const uint32_t ec = lane < 8 ? 0u : chunks - 1;
-    const uint32_t ek = 8 * ec + (lane & 7);
-    const bool edge = lane < 16 && chunks > 0 && (ec < full_lo || ec >= full_hi) && (lane < 8 || ec > 0) &&
-                      ek >= lead && ek < span;
+    // Outputs in the 64-byte sectors (32 weights) that the unit shares with
+    // its neighbours go out element by element through the cache, where the
+    // two units' parts of a sector meet: lanes 0..31 take the head sector's
+    // staged elements [lead, e1), lanes 32..63 the tail sector's [e2, span).
+    // Chunks [full_lo, full_hi) fill whole sectors and go out as 16-byte
+    // non-temporal stores.  Sector boundaries fall where base + k is a
+    // multiple of 32 (base is a multiple of 8).
+    const uint32_t b32 = static_cast<uint32_t>(base) & 31u;
+    const uint32_t hs = ((b32 + lead + 31u) & ~31u) - b32;  // first whole sector
+    const uint32_t ts = b32 + span >= 32u ? ((b32 + span) & ~31u) - b32 : 0u;  // end of the last one
+    const uint32_t e1 = hs < span ? hs : span;
+    const uint32_t e2 = ts > e1 ? ts : e1;
+    const uint32_t full_lo = e1 / 8;
+    const uint32_t full_hi = e2 / 8;
+    const uint32_t ek = lane < 32 ? lead + lane : e2 + (lane - 32u);
+    const bool edge = ek < (lane < 32 ? e1 : span);
 
     // sign/mantissa bytes of the unit, requested before decoding starts
     // (chunks past the unit read as 0); read once, so non-temporal
