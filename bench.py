@@ -3,7 +3,10 @@
 
 One step = one df11_decode_block launch over a whole transformer block (the
 Llama-3.1-8B-shaped block by default: q,k,v,o,gate,up,down, 218,103,808
-weights, one shared codebook), inputs resident in HBM.  Prints one JSON line.
+weights, one shared codebook), inputs resident in HBM.  The timed launches
+rotate over device copies of the block, as a model decodes a different block
+each time (no launch finds the previous one's sections in the caches).
+Prints one JSON line.
 
   value      decoded BF16 GB/s = 2 * weights * steps / timed seconds
   roofline   algorithmic HBM bytes per launch (compressed sections read +
@@ -25,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+INFINITY_CACHE_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 KERNEL_SRC = os.path.join(ROOT, "huffman_decode_block_amd", "csrc", "df11_decode.hip")
 # the headers of this package that the decode kernel's code includes
 KERNEL_HEADERS = [os.path.join(ROOT, "huffman_decode_block_amd", "csrc", h) for h in ("df11_wave.h", "df11_internal.h")] \
@@ -413,15 +417,30 @@ def main():
     launch = (args.waves, args.max_groups, args.variant, args.oversubscribe) \
         if (args.waves or args.max_groups or args.variant or args.oversubscribe) else None
     stream = torch.cuda.current_stream(dev)
+    ab = algorithmic_bytes(s, with_counts)
+
+    # A model decodes a different block each time.  The timed launches rotate
+    # over device copies of the block (each with its own sections and output)
+    # whose sections together are at least twice the 256 MiB Infinity Cache,
+    # so no launch finds what the one before it read still cached; decoding
+    # one block over and over would find part of it there.
+    n_copies = max(2, -(-2 * INFINITY_CACHE_BYTES // ab["read"]))
+    copies = [(blk, out)] + [(hdb.DeviceBlock.from_encoded(enc, device=dev), torch.empty_like(out))
+                             for _ in range(n_copies - 1)]
+
+    def decode(i):
+        b, o = copies[i % n_copies]
+        hdb.df11_decode_block(b, out=o, stream=stream, launch=launch)
 
     # Correctness of what is timed, checked first: the copy it needs would
     # leave the GPU idle (and its clocks falling) right before the timed steps.
-    hdb.df11_decode_block(blk, out=out, stream=stream, launch=launch)
     xd = torch.from_numpy(x.view(np.int16)).to(dev)
-    if not torch.equal(out.view(torch.int16), xd):
-        raise SystemExit("decode is not bit-exact; refusing to report a number")
+    for i in range(n_copies):
+        decode(i)
+        if not torch.equal(copies[i][1].view(torch.int16), xd):
+            raise SystemExit("decode is not bit-exact; refusing to report a number")
     del xd
-    progress("decode checked bit-exact; timing")
+    progress(f"decode checked bit-exact on {n_copies} device copies of the block; timing")
     region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -429,32 +448,44 @@ def main():
     # Untimed pre-warm until the clocks have ramped (not counted as steps),
     # then the W warmup steps, then the K timed steps with no idle between.
     t_pre = time.perf_counter()
+    i = 0
     while (time.perf_counter() - t_pre) * 1e3 < args.prewarm_ms:
         for _ in range(50):
-            hdb.df11_decode_block(blk, out=out, stream=stream, launch=launch)
+            decode(i)
+            i += 1
         torch.cuda.synchronize()
     for _ in range(args.warmup):
-        hdb.df11_decode_block(blk, out=out, stream=stream, launch=launch)
+        decode(i)
+        i += 1
     torch.cuda.synchronize()
     # The timed region: K launches back to back on the decode's stream, HIP
     # events at its two ends (the kernel's average launch duration is their
     # interval over K).
     t0 = time.perf_counter()
     region[0].record(stream)
-    for i in range(args.steps):
-        hdb.df11_decode_block(blk, out=out, stream=stream, launch=launch)
+    for k in range(args.steps):
+        decode(i + k)
     region[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     k_avg = region[0].elapsed_time(region[1]) * 1e-3 / args.steps
+    i += args.steps
     # Spread of single launches, from K more launches each between its own
     # pair of events (the event pair adds a few microseconds to each).
-    for i in range(args.steps):
-        starts[i].record(stream)
-        hdb.df11_decode_block(blk, out=out, stream=stream, launch=launch)
-        ends[i].record(stream)
+    for k in range(args.steps):
+        starts[k].record(stream)
+        decode(i + k)
+        ends[k].record(stream)
     torch.cuda.synchronize()
     kt = sorted(a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends))
+    # For comparison, K launches that decode the first copy over and over
+    # (part of its sections is then still in the Infinity Cache).
+    region[0].record(stream)
+    for k in range(args.steps):
+        decode(0)
+    region[1].record(stream)
+    torch.cuda.synchronize()
+    k_same = region[0].elapsed_time(region[1]) * 1e-3 / args.steps
     # Cold single launches: before each, a read of 1 GiB of unrelated data
     # pushes the block's sections out of the L2 and the Infinity Cache, leaving
     # clean lines (not in any interval).  An int64 sum reads its input as it
@@ -462,22 +493,22 @@ def main():
     scratch = torch.ones(1 << 27, dtype=torch.int64, device=dev)
     cold = []
     ce = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    for i in range(args.cold_launches):
+    for k in range(args.cold_launches):
         flush = scratch.sum()
         ce[0].record(stream)
-        hdb.df11_decode_block(blk, out=out, stream=stream, launch=launch)
+        decode(0)
         ce[1].record(stream)
         torch.cuda.synchronize()
         cold.append(ce[0].elapsed_time(ce[1]) * 1e-3)
     del scratch, flush
     cold.sort()
-    xd = torch.from_numpy(x.view(np.int16)).to(dev)  # and of the last timed decode
-    if not torch.equal(out.view(torch.int16), xd):
-        raise SystemExit("decode is not bit-exact after timing; refusing to report a number")
-    del xd
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)  # and of every copy's last decode
+    for b, o in copies:
+        if not torch.equal(o.view(torch.int16), xd):
+            raise SystemExit("decode is not bit-exact after timing; refusing to report a number")
+    del xd, copies
 
     n = int(s.n_total)
-    ab = algorithmic_bytes(s, with_counts)
     achieved = ab["total"] / k_avg / 1e9
     value = 2.0 * n * args.steps / wall / 1e9
     # the committed counters were taken on the default (multi-code) kernel
@@ -528,7 +559,9 @@ def main():
                       "cold_single_launch": {"p10": round(cold[len(cold) // 10] * 1e6, 2),
                                              "p50": round(cold[len(cold) // 2] * 1e6, 2),
                                              "p90": round(cold[(9 * len(cold)) // 10] * 1e6, 2),
-                                             "launches": len(cold)} if cold else None},
+                                             "launches": len(cold)} if cold else None,
+                      "same_block_back_to_back": round(k_same * 1e6, 2),
+                      "device_copies_rotated": n_copies},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
