@@ -267,9 +267,12 @@ def overlap_bench(args, dev) -> None:
     x = di.generate(args.workload)
     enc = hdb.df11_encode_block(di.split(args.workload, x))
     blk = hdb.DeviceBlock.from_encoded(enc, device=dev)
+    # two device copies of the block in turn, so that no decode finds the
+    # previous one's sections in the Infinity Cache (as with different blocks)
+    blks = [blk, hdb.DeviceBlock.from_encoded(enc, device=dev)]
     shapes = [(m.rows, m.cols) for m in wl.mats]
     nb = args.overlap_blocks
-    ahead = DecodeAhead([blk] * nb, [shapes] * nb, device=dev)  # the same block nb times
+    ahead = DecodeAhead([blks[i % 2] for i in range(nb)], [shapes] * nb, device=dev)
     ref = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
     ref_views = hdb.matrix_views(ref, blk, shapes)
     stream = torch.cuda.current_stream(dev)
@@ -302,8 +305,8 @@ def overlap_bench(args, dev) -> None:
                 consume(i, ref_views)
 
         def decodes_only():
-            for _ in range(nb):
-                hdb.df11_decode_block(blk, out=ahead.bufs[0][: blk.n_total], stream=stream)
+            for i in range(nb):
+                hdb.df11_decode_block(blks[i % 2], out=ahead.bufs[i % 2][: blk.n_total], stream=stream)
 
         for f in (gemms_only, decodes_only):  # warm up (clocks, GEMM algorithm choice)
             for _ in range(3):
