@@ -97,6 +97,13 @@ def measured_traffic(workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
+def rotation_copies(read_bytes: int, cap: int = 64) -> int:
+    """Device copies of a block that the timed launches rotate over: enough
+    that their sections add up to twice the Infinity Cache, at least 2, at most
+    `cap` (blocks so small that the cap binds stay cached whatever the count)."""
+    return int(min(cap, max(2, -(-2 * INFINITY_CACHE_BYTES // max(int(read_bytes), 1)))))
+
+
 def progress(msg: str) -> None:
     """A progress line on stderr (stdout carries only the result line)."""
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -427,7 +434,7 @@ def main():
     # whose sections together are at least twice the 256 MiB Infinity Cache,
     # so no launch finds what the one before it read still cached; decoding
     # one block over and over would find part of it there.
-    n_copies = max(2, -(-2 * INFINITY_CACHE_BYTES // ab["read"]))
+    n_copies = rotation_copies(ab["read"])
     copies = [(blk, out)] + [(hdb.DeviceBlock.from_encoded(enc, device=dev), torch.empty_like(out))
                              for _ in range(n_copies - 1)]
 

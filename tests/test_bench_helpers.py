@@ -97,3 +97,15 @@ def test_algorithmic_bytes_are_integers(bench):
     enc = hdb.df11_encode_block([np.zeros(1000, np.uint16)])
     ab = bench.algorithmic_bytes(enc.sections)
     assert all(isinstance(v, int) for v in ab.values())
+
+
+def test_rotation_copies_exceed_twice_the_infinity_cache():
+    import bench
+    cache = bench.INFINITY_CACHE_BYTES
+    assert bench.rotation_copies(299_316_096) == 2          # a Llama-3.1-8B-shaped block's sections
+    assert bench.rotation_copies(22_768_000) == 24          # one 4096 x 4096 matrix
+    for read in (1_000_000, 22_768_000, 100_000_000, 299_316_096, 4_000_000_000):
+        k = bench.rotation_copies(read)
+        assert k >= 2 and (k * read >= 2 * cache or k == 64)
+        assert k == 2 or (k - 1) * read < 2 * cache       # no more copies than needed
+    assert bench.rotation_copies(1) == 64 and bench.rotation_copies(0) == 64
