@@ -130,7 +130,12 @@ typedef struct df11_sections {
     uint64_t off_unit_end;
 } df11_sections;
 
-/* Encodes the concatenation of n_mats BF16 matrices with one shared codebook.
+/* Encodes the concatenation of n_mats BF16 matrices with one shared codebook
+ * (hada.io summary of the DFloat11 paper: section "Le format DFloat11" for
+ * the exponent histogram, the Huffman code, EncodedExponent and
+ * PackedSignMantissa; section "Noyau GPU en deux etapes et metadonnees
+ * auxiliaires" for the per-window gaps and stored output positions; section
+ * "Decompression par bloc transformer" for one codebook per block).
  * mats: host views, caller-owned, read only.  n_threads: host threads to use
  * (0 = all CPUs the process may run on).  *out receives a new blob that the
  * caller releases with df11_encoded_free.  n_mats may be 0 and views may be
@@ -219,7 +224,14 @@ df11_status df11_device_block_from_blob(const df11_sections *s, const void *devi
                                         df11_device_block *out);
 
 /* Decodes the block into out_bf16[0 .. n_total) (device memory, 16-byte
- * aligned, out_capacity elements).  One kernel launch on the HIP stream
+ * aligned, out_capacity elements): the two-phase kernel of the hada.io
+ * summary of the DFloat11 paper, section "Noyau GPU en deux etapes et
+ * metadonnees auxiliaires" (count, prefix sum, decode into an on-chip buffer,
+ * coalesced write), with the compact hierarchical tables of section
+ * "Decodage fonde sur des LUT hierarchiques" in LDS, over every matrix of a
+ * transformer block at once (section "Decompression par bloc transformer").
+ * The result is the original BF16 bits (chatpaper.ai abstract of the paper:
+ * bit-for-bit identical output).  One kernel launch on the HIP stream
  * `hip_stream` (a hipStream_t; NULL = the null stream); the call does not
  * synchronize and allocates nothing.  Exactly n_total elements are written;
  * nothing else is touched.  Argument, capacity, alignment and version errors
@@ -265,6 +277,34 @@ typedef struct df11_launch {
 df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf16,
                                  uint64_t out_capacity, void *hip_stream,
                                  const df11_launch *launch);
+
+/* ---- Bandwidth references (measurement aids) -----------------------------
+ * Two streaming kernels that move the HBM bytes of one df11_decode_block
+ * launch of blk, without decoding, so that the decode's rate can be set
+ * against what the same traffic reaches on the same GPU.  The decode reads
+ * the compressed sections once and writes the block once, coalesced (hada.io
+ * summary of the DFloat11 paper, section "Noyau GPU en deux etapes et
+ * metadonnees auxiliaires").  Both write out_bf16[i] = the block's weight i
+ * with its exponent field zero (sign and mantissa from sign_mant), for i in
+ * [0, n_total), and nothing else.
+ *  DF11_REFERENCE_SKELETON: the decode's own HBM accesses unit by unit (one
+ *    64-lane wave per unit of 64 windows: window words with their halo, gap
+ *    bytes and the unit's positions one unit ahead, 8-byte sign/mantissa
+ *    loads, 16-byte non-temporal stores of whole 64-byte sectors, 2-byte
+ *    stores of sectors shared with the neighbouring units), with the
+ *    decode's workgroup size and grid rule.
+ *  DF11_REFERENCE_STREAM: the same byte counts moved in whole tiles of 4,096
+ *    weights per wave (no unit boundaries, no shared sectors).
+ * Same arguments, checks, errors and stream semantics as df11_decode_block_ex
+ * (launch: waves_per_group, max_groups and oversubscribe are used; variant is
+ * ignored; NULL = automatic).  Blocks with stored window counts or the
+ * aligned-units layout: DF11_E_UNSUPPORTED; an unknown kind:
+ * DF11_E_INVALID_ARG. */
+#define DF11_REFERENCE_SKELETON 1u
+#define DF11_REFERENCE_STREAM 2u
+
+df11_status df11_bandwidth_reference(const df11_device_block *blk, uint16_t *out_bf16, uint64_t out_capacity,
+                                     uint32_t kind, void *hip_stream, const df11_launch *launch);
 
 /* ---- GPU-side encoder ---------------------------------------------------
  * The step before the decode, for a block whose BF16 weights are already in
