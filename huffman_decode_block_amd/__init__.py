@@ -108,7 +108,11 @@ EXPORTS = [
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
     "df11_gpu_chunk_hist_bytes", "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode",
+    "df11_bandwidth_reference",
 ]
+
+DF11_REFERENCE_SKELETON = 1
+DF11_REFERENCE_STREAM = 2
 
 
 def lib():
@@ -118,6 +122,11 @@ def lib():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with python -m huffman_decode_block_amd.build")
+    from .build import built_stamp, source_stamp
+    have, want = built_stamp(), source_stamp()
+    if have != want:
+        raise ImportError(f"{LIB_PATH} was built from other sources (stamp {have}, sources {want}): "
+                          "rebuild it with python -m huffman_decode_block_amd.build")
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     L.df11_encode_block.argtypes = [P(df11_bf16_view), _u32, _u32, P(_vp)]
@@ -148,6 +157,8 @@ def lib():
     L.df11_gpu_encode.restype = ctypes.c_int32
     L.df11_decode_block_ex.argtypes = [P(df11_device_block), _vp, _u64, _vp, P(df11_launch)]
     L.df11_decode_block_ex.restype = ctypes.c_int32
+    L.df11_bandwidth_reference.argtypes = [P(df11_device_block), _vp, _u64, _u32, _vp, P(df11_launch)]
+    L.df11_bandwidth_reference.restype = ctypes.c_int32
     L.df11_status_str.argtypes = [ctypes.c_int32]
     L.df11_status_str.restype = ctypes.c_char_p
     L.df11_last_hip_error.argtypes = []
@@ -156,6 +167,13 @@ def lib():
     L.df11_hip_error_name.restype = ctypes.c_char_p
     _lib = L
     return L
+
+
+def library_stamp() -> str:
+    """The source stamp of the loaded library (see the build module)."""
+    lib()
+    from .build import built_stamp
+    return built_stamp()
 
 
 def df11_status_str(status: int) -> str:
@@ -458,6 +476,25 @@ def df11_decode_block_ex(block: DeviceBlock, out=None, stream=None, waves_per_gr
     return df11_decode_block(block, out, stream, launch=(waves_per_group, max_groups, variant, oversubscribe))
 
 
+def df11_bandwidth_reference(block: DeviceBlock, out, kind: int, stream=None, launch=None):
+    """A bandwidth reference for the decode of `block` (DF11_REFERENCE_SKELETON
+    or DF11_REFERENCE_STREAM): moves the decode's HBM bytes and writes into
+    `out` (a 16-bit device tensor) each weight with its exponent field zero.
+    Returns out."""
+    import torch
+    if out.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not out.is_cuda:
+        raise TypeError("out must be a 16-bit device tensor")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    L = None if launch is None else (launch if isinstance(launch, df11_launch) else df11_launch(*launch))
+    with torch.cuda.device(out.device):
+        st = lib().df11_bandwidth_reference(ctypes.byref(block.raw), out.data_ptr(), out.numel(), int(kind),
+                                            _stream_handle(stream, out.device),
+                                            None if L is None else ctypes.byref(L))
+    _check(st, "df11_bandwidth_reference")
+    return out
+
+
 def df11_gpu_chunk_hist_bytes(n: int) -> int:
     """Bytes of the per-chunk exponent counts of n weights (256 uint16 per 4,096 weights)."""
     return int(lib().df11_gpu_chunk_hist_bytes(int(n)))
@@ -593,7 +630,7 @@ __all__ = [
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
     "df11_gpu_chunk_hist_bytes", "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode", "gpu_encode",
-    "GpuEncoded",
+    "GpuEncoded", "df11_bandwidth_reference", "DF11_REFERENCE_SKELETON", "DF11_REFERENCE_STREAM",
     "Encoded", "Sections",
-    "DeviceBlock", "DF11Error", "matrix_views", "lib",
+    "DeviceBlock", "DF11Error", "matrix_views", "lib", "library_stamp",
 ]
