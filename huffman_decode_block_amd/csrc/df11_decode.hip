@@ -61,6 +61,7 @@ struct KParams {
     uint32_t last_unit_bits;  // stream bits in the last unit (1..4096)
     uint32_t n_tables;
     uint32_t stage_elems;  // 16-bit staging elements per wave, multiple of 8
+    uint32_t out_phase;    // (address of out / 2) mod 32: where 64-byte sectors start
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -367,9 +368,10 @@ __device__ __forceinline__ void decode_unit(const KParams &p, const uint32_t *lu
     // two units' parts of a sector meet: lanes 0..31 take the head sector's
     // staged elements [lead, e1), lanes 32..63 the tail sector's [e2, span).
     // Chunks [full_lo, full_hi) fill whole sectors and go out as 16-byte
-    // non-temporal stores.  Sector boundaries fall where base + k is a
-    // multiple of 32 (base is a multiple of 8).
-    const uint32_t b32 = static_cast<uint32_t>(base) & 31u;
+    // non-temporal stores.  Sector boundaries fall where the address of
+    // out[base + k] is a multiple of 64 bytes (out is 16-byte aligned and
+    // base a multiple of 8, so b32 is a multiple of 8).
+    const uint32_t b32 = (p.out_phase + static_cast<uint32_t>(base)) & 31u;
     const uint32_t hs = ((b32 + lead + 31u) & ~31u) - b32;  // first whole sector
     const uint32_t ts = b32 + span >= 32u ? ((b32 + span) & ~31u) - b32 : 0u;  // end of the last one
     const uint32_t e1 = hs < span ? hs : span;
@@ -586,8 +588,6 @@ df11_decode_kernel(KParams p) {
 
 // ------------------------------------------------------------------ host side
 
-thread_local int32_t g_last_hip_error = 0;
-
 struct DeviceInfo {
     int cus = 0;
     int lds_per_group = 0;
@@ -627,7 +627,11 @@ int occupancy(const void *fn, uint32_t waves, uint32_t lds_bytes) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-df11_status check_block(const df11_device_block *b, const uint16_t *out, uint64_t cap) {
+}  // namespace
+
+thread_local int32_t df11i::last_hip_error = 0;
+
+df11_status df11i::check_device_block(const df11_device_block *b, const uint16_t *out, uint64_t cap) {
     if (!b) return DF11_E_INVALID_ARG;
     if (b->version != DF11_FORMAT_VERSION) return DF11_E_UNSUPPORTED;
     if (b->n_total == 0) return DF11_OK;
@@ -652,9 +656,7 @@ df11_status check_block(const df11_device_block *b, const uint16_t *out, uint64_
     return DF11_OK;
 }
 
-}  // namespace
-
-extern "C" int32_t df11_last_hip_error(void) { return g_last_hip_error; }
+extern "C" int32_t df11_last_hip_error(void) { return df11i::last_hip_error; }
 
 extern "C" const char *df11_hip_error_name(int32_t code) {
     return hipGetErrorName(static_cast<hipError_t>(code));
@@ -664,7 +666,7 @@ namespace {
 
 df11_status decode_block(const df11_device_block *blk, uint16_t *out_bf16, uint64_t out_capacity, void *hip_stream,
                          const df11_launch *launch) {
-    df11_status rc = check_block(blk, out_bf16, out_capacity);
+    df11_status rc = df11i::check_device_block(blk, out_bf16, out_capacity);
     if (rc != DF11_OK || blk->n_total == 0) return rc;
     const uint32_t variant = (launch && launch->variant) ? launch->variant : DF11_VARIANT_MULTI;
     if (variant != DF11_VARIANT_SINGLE && variant != DF11_VARIANT_MULTI && variant != DF11_VARIANT_COUNTS)
@@ -737,6 +739,7 @@ df11_status decode_block(const df11_device_block *blk, uint16_t *out_bf16, uint6
     p.last_unit_bits = static_cast<uint32_t>(blk->total_bits - 4096 * (blk->n_units - 1));
     p.n_tables = blk->n_tables;
     p.stage_elems = stage_elems;
+    p.out_phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(out_bf16) >> 1) & 31u;
 
     // The automatic grid gives each wave about four units to walk, whatever
     // the block's size (one persistent wave of workgroups streams worse, and so
@@ -758,7 +761,7 @@ df11_status decode_block(const df11_device_block *blk, uint16_t *out_bf16, uint6
     const hipError_t err = hipLaunchKernel(fn, dim3(static_cast<uint32_t>(grid)), dim3(64 * waves), args,
                                            lds_bytes, static_cast<hipStream_t>(hip_stream));
     if (err != hipSuccess) {
-        g_last_hip_error = static_cast<int32_t>(err);
+        df11i::last_hip_error = static_cast<int32_t>(err);
         return DF11_E_HIP;
     }
     return DF11_OK;

@@ -496,8 +496,6 @@ __global__ void __launch_bounds__(kThreads) finish_kernel(EncParams p) {
             p.counts[w] = static_cast<uint8_t>(p.wfirst[w + 1] - p.wfirst[w]);
 }
 
-thread_local int32_t g_last_hip_error = 0;
-
 uint64_t align256(uint64_t v) { return (v + 255) / 256 * 256; }
 
 struct Workspace {
@@ -578,7 +576,7 @@ extern "C" df11_status df11_gpu_histogram(const uint16_t *x, uint64_t n, uint64_
         err = launch(hist_kernel, static_cast<uint32_t>(std::min<uint64_t>(n_chunks, 2048)), kThreads, st, x, n,
                      hist, chunk_hist);
     if (err != hipSuccess) {
-        g_last_hip_error = static_cast<int32_t>(err);
+        df11i::last_hip_error = static_cast<int32_t>(err);
         return DF11_E_HIP;
     }
     return DF11_OK;
@@ -679,7 +677,7 @@ df11_status gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint1
     }
     if (err == hipSuccess && nw) err = launch(finish_kernel, grid_for(nw / 8 + 1, 4096), kThreads, st, p);
     if (err != hipSuccess) {
-        g_last_hip_error = static_cast<int32_t>(err);
+        df11i::last_hip_error = static_cast<int32_t>(err);
         return DF11_E_HIP;
     }
     return DF11_OK;

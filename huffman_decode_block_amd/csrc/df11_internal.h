@@ -91,6 +91,17 @@ uint32_t thread_count(uint32_t requested);
 df11_status code_lengths_for(const uint64_t cnt[256], uint8_t code_len[256], uint32_t *max_len,
                              uint32_t *n_symbols, uint64_t *total_bits);
 
+// Host checks of a device block and its output before a launch: version,
+// pointers, capacity, 16-byte alignment, sizes that no encoder produces
+// (more than 2^48 weights, fewer than 1 or more than 32 bits per weight, 64
+// with the aligned layout's filler), section sizes against n_total and
+// total_bits.  n_total = 0 passes with only the version checked.
+df11_status check_device_block(const df11_device_block *b, const uint16_t *out, uint64_t cap);
+
+// The HIP error code of the last failing launch in this thread, for every
+// entry point that launches kernels (reported by df11_last_hip_error).
+extern thread_local int32_t last_hip_error;
+
 }  // namespace df11i
 
 struct df11_encoded {

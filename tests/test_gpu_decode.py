@@ -38,16 +38,19 @@ def oracle_view(s):
                           max_len=int(s.max_code_len))
 
 
-def decode_guarded(torch, blk, n, poison, launch=None, stream=None):
-    buf = torch.full((n + 2 * GUARD,), poison, dtype=torch.int16, device="cuda")
-    view = buf[GUARD:GUARD + n]
+def decode_guarded(torch, blk, n, poison, launch=None, stream=None, lead=GUARD):
+    """Decodes into a view `lead` elements into a poisoned buffer (torch's
+    allocations start on 512-byte boundaries, so lead = GUARD puts the output
+    on a 64-byte boundary, GUARD + 8k on a 16k-byte offset from one)."""
+    buf = torch.full((n + lead + GUARD,), poison, dtype=torch.int16, device="cuda")
+    view = buf[lead:lead + n]
     hdb.df11_decode_block(blk, out=view, stream=stream, launch=launch)
     torch.cuda.synchronize()
     h = buf.cpu().numpy().view(np.uint16)
     p = np.uint16(poison & 0xFFFF)
-    assert (h[:GUARD] == p).all(), "write below the output"
-    assert (h[GUARD + n:] == p).all(), "write past the output"
-    return h[GUARD:GUARD + n].copy()
+    assert (h[:lead] == p).all(), "write below the output"
+    assert (h[lead + n:] == p).all(), "write past the output"
+    return h[lead:lead + n].copy()
 
 
 def check_oracle_sections(torch, x, name, variants=(0,)):
@@ -138,6 +141,21 @@ def test_launch_geometry_does_not_change_the_output(torch, waves, max_groups, ov
                        launch=(waves, max_groups, variant, over))
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("offset_bytes", [16, 32, 48])
+def test_output_off_a_64_byte_boundary(torch, offset_bytes, variant):
+    """Outputs that start 16, 32 or 48 bytes past a 64-byte boundary (a view
+    such as big[8:]): the kernel finds the 64-byte sectors it shares with
+    neighbouring units from the output's address, and the result is the
+    same."""
+    x = di.random_normal(1_000_003, 0.02, 90 + offset_bytes)
+    enc = hdb.df11_encode_block([x], window_counts=True)
+    blk = hdb.DeviceBlock.from_encoded(enc)
+    say(f"output offset {offset_bytes} B, variant {variant}")
+    y = decode_guarded(torch, blk, x.size, 0x5A5A, launch=(0, 0, variant), lead=GUARD + offset_bytes // 2)
+    np.testing.assert_array_equal(y, x)
+
+
 def test_workload_c2(torch):
     x = di.generate("C2")
     check_oracle_sections(torch, x, "C2", VARIANTS)
@@ -224,7 +242,7 @@ def test_workload_c3_full(torch):
 
 
 def test_workload_c4_full(torch):
-    _full_block(torch, "C4", (hdb.DF11_VARIANT_MULTI, hdb.DF11_VARIANT_COUNTS))
+    _full_block(torch, "C4", VARIANTS)
 
 
 def test_workload_c5_full(torch):
