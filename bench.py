@@ -3,14 +3,20 @@
 
 One step = one df11_decode_block launch over a whole transformer block (the
 Llama-3.1-8B-shaped block by default: q,k,v,o,gate,up,down, 218,103,808
-weights, one shared codebook), inputs resident in HBM.  The timed launches
-rotate over device copies of the block, as a model decodes a different block
-each time (no launch finds the previous one's sections in the caches).
-Prints one JSON line.
+weights, one shared codebook), inputs resident in HBM, with the caches
+flushed before it: a read of 1 GiB of unrelated data pushes the block out of
+the L2s and the 256 MB Infinity Cache, as a model's other work does between
+two block decodes.  Flush and decode pairs are enqueued back to back with no
+host synchronisation; each decode is timed by its own HIP event pair.  The
+launches rotate over device copies of the block.  Prints one JSON line.
 
-  value      decoded BF16 GB/s = 2 * weights * steps / timed seconds
+  value      decoded BF16 GB/s = 2 * weights / mean decode time
   roofline   algorithmic HBM bytes per launch (compressed sections read +
-             BF16 written) / average kernel time from HIP events, vs 8 TB/s
+             BF16 written) / mean decode time, vs 8 TB/s; frac_rotated is the
+             same for launches back to back over the copies without flushes
+  bandwidth_reference  two streaming kernels of the library that move the
+             decode's bytes without decoding (its memory skeleton, and a plain
+             stream of the same bytes), timed in both schedules
   cpu_baseline  the oracle's unit-parallel bit-serial decode of the same block
              on this host's cores (rank 0, N=1 only)
 """
@@ -36,29 +42,7 @@ KERNEL_HEADERS = [os.path.join(ROOT, "huffman_decode_block_amd", "csrc", h) for 
 COUNTERS = os.path.join(ROOT, "profiles", "df11_decode_kernel_c3_hbm_counters.json")
 
 
-def code_tokens(src: str) -> str:
-    """The source with comments removed and whitespace runs collapsed, so that
-    a change of comments alone keeps the kernel's identity."""
-    out, i, n = [], 0, len(src)
-    while i < n:
-        c = src[i]
-        if src.startswith("//", i):
-            i = src.find("\n", i)
-            i = n if i < 0 else i
-        elif src.startswith("/*", i):
-            j = src.find("*/", i + 2)
-            i = n if j < 0 else j + 2
-            out.append(" ")
-        elif c in "\"'":
-            j = i + 1
-            while j < n and src[j] != c:
-                j += 2 if src[j] == "\\" else 1
-            out.append(src[i:j + 1])
-            i = j + 1
-        else:
-            out.append(c)
-            i += 1
-    return " ".join("".join(out).split())
+from huffman_decode_block_amd.build import code_tokens  # noqa: E402  (re-exported for the tests)
 
 
 def kernel_hash() -> str:
@@ -109,26 +93,53 @@ def progress(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def copy_context(n_bytes: int, dev, reps: int = 20) -> dict:
-    """A plain device-to-device copy that moves the same HBM bytes as one
-    decode (half read, half written), timed the same way: the achievable
-    streaming rate on this GPU, reported as context for the decode's rate."""
+def pctl(v, q: float) -> float:
+    """The q-quantile of a list (nearest rank)."""
+    v = sorted(v)
+    return v[min(len(v) - 1, int(q * len(v)))]
+
+
+class ColdSchedule:
+    """Steps that each start with the caches flushed: a read of 1 GiB of
+    unrelated data (an int64 sum, which torch runs on its input as it is; a
+    write would leave dirty lines whose write-back competes with the step)
+    pushes everything out of the L2s and the 256 MB Infinity Cache, then the
+    launch runs between its own pair of HIP events on the same stream.  Pairs
+    are enqueued back to back with no host synchronisation, so the GPU never
+    idles and its clocks stay up; one synchronize at the end."""
+
+    FLUSH_BYTES = 1 << 30
+
+    def __init__(self, dev, stream):
+        import torch
+        self.torch = torch
+        self.stream = stream
+        self.scratch = torch.ones(self.FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+
+    def run(self, launch, k: int) -> list:
+        """k steps of launch(i); returns each launch's duration in seconds."""
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+        for i in range(k):
+            self.scratch.sum()
+            ev[i][0].record(self.stream)
+            launch(i)
+            ev[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e-3 for a, b in ev]
+
+
+def back_to_back(launch, k: int, stream, start: int = 0) -> float:
+    """k launches back to back between one pair of HIP events on `stream`;
+    returns the average launch duration in seconds."""
     import torch
-    half = max(16, n_bytes // 2 // 16 * 16)
-    src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(5):
-        dst.copy_(src)
-    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    ev[0].record(stream)
-    for _ in range(reps):
-        dst.copy_(src)
-    ev[1].record(stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(k):
+        launch(start + i)
+    b.record(stream)
     torch.cuda.synchronize()
-    t = ev[0].elapsed_time(ev[1]) * 1e-3 / reps
-    del src, dst
-    return {"bytes": 2 * half, "copy_us": round(t * 1e6, 2), "copy_GBps": round(2 * half / t / 1e9, 1)}
+    return a.elapsed_time(b) * 1e-3 / k
 
 
 def cpu_model() -> str:
@@ -382,8 +393,19 @@ def main():
                     help="untimed decodes before the warmup steps, for this long (the GPU's clocks ramp up "
                          "over the first ~10 ms of load after host-side work)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--cold-launches", type=int, default=20,
-                    help="single launches each after a read of 1 GiB of unrelated data (caches flushed)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline (cold) schedule: no back-to-back, same-block or "
+                         "bandwidth-reference legs (for profiler runs, whose per-kernel averages then "
+                         "cover the headline launches only)")
+    ap.add_argument("--schedule", default="cold", choices=["cold", "rotated"],
+                    help="the headline leg: cold = caches flushed before every launch, each launch timed by its "
+                         "own event pair; rotated = launches back to back over the device copies, one event pair "
+                         "around all of them")
+    ap.add_argument("--kernel", default="decode", choices=["decode", "skeleton", "stream"],
+                    help="what the headline leg times: the decode, or one of the library's bandwidth references "
+                         "(the line then reports that kernel, not the decode)")
+    ap.add_argument("--out-offset-bytes", type=int, default=0, choices=[0, 16, 32, 48],
+                    help="place each output this many bytes past a 64-byte boundary")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--overlap", default="",
                     help="comma-separated batch sizes: instead of the main line, measure the decode of block i+1 "
@@ -436,21 +458,22 @@ def main():
                                 aligned_units=args.aligned_units)
     s = enc.sections
     progress(f"encoded on the host in {time.perf_counter() - t_enc:.1f} s")
-    blk = hdb.DeviceBlock.from_encoded(enc, device=dev)
-    out = torch.empty(s.n_total, dtype=torch.bfloat16, device=dev)
     launch = (args.waves, args.max_groups, args.variant, args.oversubscribe) \
         if (args.waves or args.max_groups or args.variant or args.oversubscribe) else None
     stream = torch.cuda.current_stream(dev)
     ab = algorithmic_bytes(s, with_counts)
+    n = int(s.n_total)
+    off = args.out_offset_bytes // 2
 
-    # A model decodes a different block each time.  The timed launches rotate
-    # over device copies of the block (each with its own sections and output)
-    # whose sections together are at least twice the 256 MiB Infinity Cache,
-    # so no launch finds what the one before it read still cached; decoding
-    # one block over and over would find part of it there.
+    def new_output():
+        # torch's allocations start on 512-byte boundaries
+        return torch.empty(n + off, dtype=torch.bfloat16, device=dev)[off:]
+
+    # A model decodes a different block each time.  The launches rotate over
+    # device copies of the block (each with its own sections and output) whose
+    # sections together are at least twice the 256 MiB Infinity Cache.
     n_copies = rotation_copies(ab["read"])
-    copies = [(blk, out)] + [(hdb.DeviceBlock.from_encoded(enc, device=dev), torch.empty_like(out))
-                             for _ in range(n_copies - 1)]
+    copies = [(hdb.DeviceBlock.from_encoded(enc, device=dev), new_output()) for _ in range(n_copies)]
 
     def decode(i):
         b, o = copies[i % n_copies]
@@ -465,96 +488,135 @@ def main():
             raise SystemExit("decode is not bit-exact; refusing to report a number")
     del xd
     progress(f"decode checked bit-exact on {n_copies} device copies of the block; timing")
-    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
-    # Untimed pre-warm until the clocks have ramped (not counted as steps),
-    # then the W warmup steps, then the K timed steps with no idle between.
+    # The launches that can be timed: the decode and the two bandwidth
+    # references (same copies and outputs; the references write the weights
+    # with their exponent fields zero).
+    ref_launch = None if launch is None else (args.waves, args.max_groups, 0, args.oversubscribe)
+
+    def reference(kind):
+        def run(i):
+            b, o = copies[i % n_copies]
+            hdb.df11_bandwidth_reference(b, o, kind, stream=stream, launch=ref_launch)
+        return run
+
+    kernels = {"decode": decode}
+    if not args.aligned_units and not with_counts:
+        kernels["skeleton"] = reference(hdb.DF11_REFERENCE_SKELETON)
+        kernels["stream"] = reference(hdb.DF11_REFERENCE_STREAM)
+    if args.kernel not in kernels:
+        raise SystemExit("the bandwidth references cover the pages' format only")
+    cold = ColdSchedule(dev, stream)
+    pos = [0]
+
+    def leg(name, schedule, k):
+        """k timed launches of kernel `name` in `schedule`: per-launch times
+        (cold) or the region average (rotated), in seconds."""
+        fn, start = kernels[name], pos[0]
+        pos[0] += k
+        if schedule == "cold":
+            return cold.run(lambda j: fn(start + j), k)
+        return [back_to_back(fn, k, stream, start)]
+
+    # The headline leg: untimed pre-warm in the same schedule until the
+    # clocks have ramped, then W warmup steps, then K timed steps.
     t_pre = time.perf_counter()
-    i = 0
     while (time.perf_counter() - t_pre) * 1e3 < args.prewarm_ms:
-        for _ in range(50):
-            decode(i)
-            i += 1
-        torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        decode(i)
-        i += 1
+        leg(args.kernel, args.schedule, 20)
+    leg(args.kernel, args.schedule, max(args.warmup, 1))
     torch.cuda.synchronize()
-    # The timed region: K launches back to back on the decode's stream, HIP
-    # events at its two ends (the kernel's average launch duration is their
-    # interval over K).
     t0 = time.perf_counter()
-    region[0].record(stream)
-    for k in range(args.steps):
-        decode(i + k)
-    region[1].record(stream)
-    torch.cuda.synchronize()
+    kt = leg(args.kernel, args.schedule, args.steps)
     wall = time.perf_counter() - t0
-    k_avg = region[0].elapsed_time(region[1]) * 1e-3 / args.steps
-    i += args.steps
-    # Spread of single launches, from K more launches each between its own
-    # pair of events (the event pair adds a few microseconds to each).
-    for k in range(args.steps):
-        starts[k].record(stream)
-        decode(i + k)
-        ends[k].record(stream)
-    torch.cuda.synchronize()
-    kt = sorted(a.elapsed_time(b) * 1e-3 for a, b in zip(starts, ends))
-    # For comparison, K launches that decode the first copy over and over
-    # (part of its sections is then still in the Infinity Cache).
-    region[0].record(stream)
-    for k in range(args.steps):
-        decode(0)
-    region[1].record(stream)
-    torch.cuda.synchronize()
-    k_same = region[0].elapsed_time(region[1]) * 1e-3 / args.steps
-    # Cold single launches: before each, a read of 1 GiB of unrelated data
-    # pushes the block's sections out of the L2 and the Infinity Cache, leaving
-    # clean lines (not in any interval).  An int64 sum reads its input as it
-    # is (a narrower type would first be copied, i.e. written, to int64).
-    scratch = torch.ones(1 << 27, dtype=torch.int64, device=dev)
-    cold = []
-    ce = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    for k in range(args.cold_launches):
-        flush = scratch.sum()
-        ce[0].record(stream)
-        decode(0)
-        ce[1].record(stream)
-        torch.cuda.synchronize()
-        cold.append(ce[0].elapsed_time(ce[1]) * 1e-3)
-    del scratch, flush
-    cold.sort()
-    xd = torch.from_numpy(x.view(np.int16)).to(dev)  # and of every copy's last decode
-    for b, o in copies:
-        if not torch.equal(o.view(torch.int16), xd):
-            raise SystemExit("decode is not bit-exact after timing; refusing to report a number")
-    del xd, copies
+    k_head = sum(kt) / len(kt)
 
-    n = int(s.n_total)
-    achieved = ab["total"] / k_avg / 1e9
-    value = 2.0 * n * args.steps / wall / 1e9
+    other = "rotated" if args.schedule == "cold" else "cold"
+    times = {(args.kernel, args.schedule): k_head}
+    if not args.headline_only:
+        if args.kernel != "decode":
+            t = leg("decode", args.schedule, args.steps)
+            times[("decode", args.schedule)] = sum(t) / len(t)
+        leg("decode", other, 20)
+        t = leg("decode", other, args.steps)
+        times[("decode", other)] = sum(t) / len(t)
+        # The same copy over and over: for blocks that fit the Infinity
+        # Cache (C1, C2) this is the hot number.
+        times[("decode", "same")] = back_to_back(lambda k: decode(0), args.steps, stream)
+    # every copy's last decode is still bit-exact (when the decode ran last)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    if args.kernel == "decode" or not args.headline_only:
+        if args.kernel != "decode":
+            for j in range(n_copies):
+                decode(j)
+        for b, o in copies:
+            if not torch.equal(o.view(torch.int16), xd):
+                raise SystemExit("decode is not bit-exact after timing; refusing to report a number")
+    refs = {}
+    if len(kernels) > 1:
+        for name in ("skeleton", "stream"):
+            if not args.headline_only:
+                for sched in ("cold", "rotated"):
+                    if (name, sched) in times:
+                        continue
+                    leg(name, sched, 20)
+                    t = leg(name, sched, args.steps)
+                    times[(name, sched)] = sum(t) / len(t)
+            if args.headline_only and name != args.kernel:
+                continue
+            expect = torch.bitwise_and(xd, torch.tensor(-32641, dtype=torch.int16, device=dev))  # 0x807F
+            for j in range(n_copies):
+                kernels[name](j)
+            for b, o in copies:
+                if not torch.equal(o.view(torch.int16), expect):
+                    raise SystemExit(f"bandwidth reference {name} wrote wrong values; refusing to report a number")
+            del expect
+            refs[name] = {f"{sched}_us": round(times[(name, sched)] * 1e6, 2)
+                          for sched in ("cold", "rotated") if (name, sched) in times}
+    del xd, copies, cold
+    torch.cuda.empty_cache()
+    k_cold = times.get(("decode", "cold"))
+    k_rot = times.get(("decode", "rotated"))
     # the committed counters were taken on the default (multi-code) kernel
-    traffic = measured_traffic(args.workload) if args.variant in (0, 2) and not args.aligned_units else None
+    traffic = measured_traffic(args.workload) if args.kernel == "decode" and args.variant in (0, 2) \
+        and not args.aligned_units else None
     if traffic is None:
         progress("roofline.traffic is null: no committed HBM counter summary matches this kernel code, "
                  "workload and variant")
-    cc = copy_context(ab["total"], dev)
-    cc["decode_over_copy"] = round(achieved / cc["copy_GBps"], 3)
+    ref_bytes = ab["total"] - int(s.raw.tables_bytes)  # the references do not read the decode tables
+    head_bytes = ab["total"] if args.kernel == "decode" else ref_bytes
+    achieved = head_bytes / k_head / 1e9
+    frac = lambda t, nb=ab["total"]: round(nb / t / 1e9 / PEAK_HBM_GBS, 4) if t else None  # noqa: E731
+    for name, r in refs.items():
+        r["bytes"] = ref_bytes
+        for sched in ("cold", "rotated"):
+            if f"{sched}_us" in r:
+                r[f"GBps_{sched}"] = round(ref_bytes / r[f"{sched}_us"] / 1e3, 1)
+                kd = times.get(("decode", sched))
+                if kd:
+                    r[f"decode_over_reference_{sched}"] = round(ab["total"] / kd / 1e9 / r[f"GBps_{sched}"], 3)
+    us = lambda v: round(v * 1e6, 2) if v else None  # noqa: E731
+    kernel_name = {"decode": "df11_decode_kernel", "skeleton": "df11_skeleton_kernel",
+                   "stream": "df11_stream_kernel"}[args.kernel]
     res = {
-        "metric": "decoded BF16 GB/s and % HBM roofline per transformer block, 1 MI355X",
-        "value": round(value, 2),
+        "metric": "decoded BF16 GB/s and % HBM roofline per transformer block, 1 MI355X" if args.kernel == "decode"
+        else f"bandwidth reference '{args.kernel}' (moves the decode's bytes without decoding; not the decode)",
+        "value": round(2.0 * n / k_head / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round(k_head * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "u32",
         "data": "synthetic",
+        "step": ("one launch over the whole block with the caches flushed before it (a 1 GiB read); value and "
+                 "ms_per_step from the launch's own HIP event pair, the flushes outside (wall_ms_per_step "
+                 "includes them)") if args.schedule == "cold" else
+                ("one launch over the whole block, launches back to back over device copies of the block; "
+                 "value and ms_per_step from one HIP event pair around the timed launches"),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "config": {
             "workload": f"{args.workload}: {wl.description}",
             "weights": n,
@@ -567,24 +629,22 @@ def main():
             "exp_entropy_bits": round(s.exp_entropy_bits, 4),
             "max_code_len": int(s.max_code_len),
             "decode_tables": int(s.n_tables),
-            "launch": {"waves_per_group": args.waves or "default", "max_groups": args.max_groups or "auto",
+            "launch": {"kernel": args.kernel, "schedule": args.schedule,
+                       "waves_per_group": args.waves or "default", "max_groups": args.max_groups or "auto",
                        "oversubscribe": args.oversubscribe or "default",
                        "variant": {0: "default (multi-code)", 1: "one code per lookup",
                                    2: "multi-code",
                                    3: "multi-code with stored per-window counts (format variant)"}[args.variant],
-                       "layout": "aligned units (format variant)" if args.aligned_units else "the pages' format"},
+                       "layout": "aligned units (format variant)" if args.aligned_units else "the pages' format",
+                       "out_offset_bytes": args.out_offset_bytes},
         },
-        "gweights_per_s": round(n * args.steps / wall / 1e9, 2),
-        "pct_hbm_roofline": round(100.0 * ab["total"] * args.steps / wall / 1e9 / PEAK_HBM_GBS, 2),
-        "kernel_us": {"avg": round(k_avg * 1e6, 2),
-                      "single_launch": {"p10": round(kt[len(kt) // 10] * 1e6, 2),
-                                        "p50": round(kt[len(kt) // 2] * 1e6, 2),
-                                        "p90": round(kt[(9 * len(kt)) // 10] * 1e6, 2)},
-                      "cold_single_launch": {"p10": round(cold[len(cold) // 10] * 1e6, 2),
-                                             "p50": round(cold[len(cold) // 2] * 1e6, 2),
-                                             "p90": round(cold[(9 * len(cold)) // 10] * 1e6, 2),
-                                             "launches": len(cold)} if cold else None,
-                      "same_block_back_to_back": round(k_same * 1e6, 2),
+        "gweights_per_s": round(n / k_head / 1e9, 2),
+        "pct_hbm_roofline": round(100.0 * achieved / PEAK_HBM_GBS, 2),
+        "kernel_us": {args.schedule: ({"mean": us(k_head), "p10": us(pctl(kt, .1)), "p50": us(pctl(kt, .5)),
+                                       "p90": us(pctl(kt, .9)), "launches": len(kt)}
+                                      if args.schedule == "cold" else {"mean": us(k_head), "launches": args.steps}),
+                      "decode_cold": us(k_cold), "decode_rotated": us(k_rot),
+                      "decode_same_block_back_to_back": us(times.get(("decode", "same"))),
                       "device_copies_rotated": n_copies},
         "roofline": {
             "bound": "hbm",
@@ -593,10 +653,14 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": ab["total"],
-            "kernel": "df11_decode_kernel",
+            "schedule": args.schedule,
+            "frac_cold": frac(k_cold),
+            "frac_rotated": frac(k_rot),
+            "algorithmic_bytes_per_launch": head_bytes,
+            "kernel": kernel_name,
         },
-        "copy_context": cc,
+        "bandwidth_reference": refs or None,
+        "library_stamp": hdb.library_stamp(),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
