@@ -108,7 +108,7 @@ EXPORTS = [
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
     "df11_gpu_chunk_hist_bytes", "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode",
-    "df11_bandwidth_reference",
+    "df11_bandwidth_reference", "df11_gpu_encode_noalloc",
 ]
 
 DF11_REFERENCE_SKELETON = 1
@@ -157,6 +157,8 @@ def lib():
     L.df11_gpu_encode.restype = ctypes.c_int32
     L.df11_decode_block_ex.argtypes = [P(df11_device_block), _vp, _u64, _vp, P(df11_launch)]
     L.df11_decode_block_ex.restype = ctypes.c_int32
+    L.df11_gpu_encode_noalloc.argtypes = [P(df11_gpu_plan), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.df11_gpu_encode_noalloc.restype = ctypes.c_int32
     L.df11_bandwidth_reference.argtypes = [P(df11_device_block), _vp, _u64, _u32, _vp, P(df11_launch)]
     L.df11_bandwidth_reference.restype = ctypes.c_int32
     L.df11_status_str.argtypes = [ctypes.c_int32]
@@ -549,6 +551,30 @@ def df11_gpu_encode(plan: df11_gpu_plan, x, chunk_hist, stream_buf, sign_mant, g
     _check(st, "df11_gpu_encode")
 
 
+DF11_NOALLOC_WORKSPACE_BYTES = 48 << 20  # the workspace array of df11_gpu_encode_noalloc
+
+
+def df11_gpu_encode_noalloc(plan: df11_gpu_plan, x, chunk_hist, stream_buf, sign_mant, gaps, unit_pos, counts,
+                            stream=None) -> None:
+    """df11_gpu_encode without a workspace argument: the library's own device
+    array serves (no device memory is allocated)."""
+    import torch
+    _device_tensor(x, "x", 2 * int(plan.n_total), sixteen_bit=True)
+    need = {"stream_buf": (stream_buf, plan.stream_bytes), "sign_mant": (sign_mant, plan.sign_mant_bytes),
+            "gaps": (gaps, plan.gaps_bytes), "unit_pos": (unit_pos, plan.unit_pos_bytes),
+            "counts": (counts, plan.counts_bytes),
+            "chunk_hist": (chunk_hist, df11_gpu_chunk_hist_bytes(int(plan.n_total)))}
+    for name, (t, nbytes) in need.items():
+        if t is not None:
+            _device_tensor(t, name, int(nbytes), dev=x.device)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    with torch.cuda.device(x.device):
+        st = lib().df11_gpu_encode_noalloc(ctypes.byref(plan), ptr(x), ptr(chunk_hist), ptr(stream_buf),
+                                           ptr(sign_mant), ptr(gaps), ptr(unit_pos), ptr(counts),
+                                           _stream_handle(stream, x.device))
+    _check(st, "df11_gpu_encode_noalloc")
+
+
 class GpuEncoded:
     """A block encoded on the device: its plan, the section tensors and a
     DeviceBlock ready for df11_decode_block."""
@@ -630,7 +656,7 @@ __all__ = [
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
     "df11_gpu_chunk_hist_bytes", "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode", "gpu_encode",
-    "GpuEncoded", "df11_bandwidth_reference", "DF11_REFERENCE_SKELETON", "DF11_REFERENCE_STREAM",
+    "GpuEncoded", "df11_bandwidth_reference", "df11_gpu_encode_noalloc", "DF11_NOALLOC_WORKSPACE_BYTES", "DF11_REFERENCE_SKELETON", "DF11_REFERENCE_STREAM",
     "Encoded", "Sections",
     "DeviceBlock", "DF11Error", "matrix_views", "lib", "library_stamp",
 ]

@@ -517,6 +517,37 @@ Workspace workspace_layout(uint64_t n, uint64_t n_windows, bool counts) {
 
 uint64_t chunk_hist_bytes(uint64_t n) { return (n + kChunk - 1) / kChunk * 256 * sizeof(uint16_t); }
 
+// Workspace of df11_gpu_encode_noalloc: one file-scope device array per GPU
+// (it lives as long as the process), for callers that cannot allocate.  In
+// host code its name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, taken once per device.
+constexpr uint64_t kScratchBytes = DF11_NOALLOC_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The current device's address of `scratch`, or null (the HIP error is then
+// recorded).
+void *scratch_address() {
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess || dev < 0 || dev >= 64) {
+        df11i::last_hip_error = static_cast<int32_t>(err != hipSuccess ? err : hipErrorInvalidDevice);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !ptr) {
+            df11i::last_hip_error = static_cast<int32_t>(err != hipSuccess ? err : hipErrorInvalidSymbol);
+            return nullptr;
+        }
+        addr[dev] = ptr;
+    }
+    return addr[dev];
+}
+
 bool aligned(const void *ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
 // hipLaunchKernel reports the status of this launch only (hipGetLastError
@@ -687,6 +718,25 @@ df11_status gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint1
 
 extern "C" df11_status df11_gpu_plan_build(const uint64_t hist[256], uint32_t flags, df11_gpu_plan *plan) {
     return df11i::guarded([&] { return plan_build(hist, flags, plan); });
+}
+
+extern "C" df11_status df11_gpu_encode_noalloc(const df11_gpu_plan *plan, const uint16_t *x,
+                                               const uint16_t *chunk_hist, uint8_t *stream, uint8_t *sign_mant,
+                                               uint8_t *gaps, uint64_t *unit_pos, uint8_t *counts,
+                                               void *hip_stream) {
+    return df11i::guarded([&]() -> df11_status {
+        if (!plan) return DF11_E_INVALID_ARG;
+        if (plan->n_total > kMaxWeights || plan->total_bits > uint64_t{DF11_MAX_CODE_LEN} * plan->n_total)
+            return DF11_E_INVALID_ARG;
+        // the workspace this plan needs, from its own sizes (not from its
+        // workspace_bytes field), against the array's size
+        const bool with_counts = (plan->flags & DF11_ENCODE_WINDOW_COUNTS) != 0;
+        const uint64_t nw = (plan->total_bits + 63) / 64;
+        if (workspace_layout(plan->n_total, nw, with_counts).bytes > kScratchBytes) return DF11_E_BUFFER_TOO_SMALL;
+        void *ws = scratch_address();
+        if (!ws) return DF11_E_HIP;
+        return gpu_encode(plan, x, chunk_hist, stream, sign_mant, gaps, unit_pos, counts, ws, hip_stream);
+    });
 }
 
 extern "C" df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint16_t *chunk_hist,

@@ -368,6 +368,26 @@ df11_status df11_gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const 
                             uint8_t *stream, uint8_t *sign_mant, uint8_t *gaps, uint64_t *unit_pos,
                             uint8_t *counts, void *workspace, void *hip_stream);
 
+/* df11_gpu_encode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without `workspace`, and the same output.  The
+ * workspace is a device array inside the library, one per GPU, of
+ * DF11_NOALLOC_WORKSPACE_BYTES (48 MiB: at 2.7 bits per exponent code,
+ * enough for about 1.1 G weights without window counts, 130 M with them),
+ * held from the first call on a GPU until the process ends.  No call allocates or frees device memory.
+ * Plans that need more workspace: DF11_E_BUFFER_TOO_SMALL, before anything
+ * is launched.  Every call on one GPU uses that GPU's array: calls whose work
+ * overlaps on one GPU (different streams, or host threads without ordering
+ * between their streams) race and must not be made; stream-ordered calls are
+ * safe.  Nothing needs clearing between calls (every workspace word is written
+ * before it is read).  Otherwise as df11_gpu_encode (DF11_E_HIP also when
+ * the array's address cannot be found). */
+#define DF11_NOALLOC_WORKSPACE_BYTES (48ull << 20)
+
+df11_status df11_gpu_encode_noalloc(const df11_gpu_plan *plan, const uint16_t *x, const uint16_t *chunk_hist,
+                                    uint8_t *stream, uint8_t *sign_mant, uint8_t *gaps, uint64_t *unit_pos,
+                                    uint8_t *counts, void *hip_stream);
+
 /* Text for a status code (static storage). */
 const char *df11_status_str(df11_status s);
 
