@@ -488,81 +488,12 @@ struct WavesPerEU {
     static constexpr int value = kDeepGlobal ? 4 : 8;
 };
 
+// The unit loop of one wave: decode unit u, then every stride-th unit after
+// it.  `cur` holds unit u's inputs, already requested.
 template <bool kDeepGlobal, bool kMulti, bool kCounts>
-__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WavesPerEU<kDeepGlobal>::value)))
-df11_decode_kernel(KParams p) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    // dynamic LDS: hierarchical tables, then one staging area per wave
-    const uint32_t lds_tables = kDeepGlobal ? 1u : p.n_tables;
-    uint32_t *lut = reinterpret_cast<uint32_t *>(lds);
-
-    uint32_t lane = threadIdx.x & 63u;
-    // wave index and wave count are uniform: keep unit indices in scalar registers
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
-    uint64_t u = uniform_u64(uint64_t{blockIdx.x} * waves + wave);
-    const uint64_t last = p.n_units - 1;  // the host launches only for blocks with weights
-    // The first unit's inputs are requested before the tables are copied, so
-    // that the two memory latencies overlap (a wave with no unit loads the
-    // last one and leaves after the workgroup barrier).
-    UnitInputs cur;
-    load_unit<kCounts>(p, u < last ? u : last, lane, cur);
-    // The tables go to LDS in one pass: every thread requests its 16-byte
-    // pieces (up to two per round) before it stores any, so their latencies
-    // overlap.  The multi-code tables are checked in registers on the way:
-    // every count entry advances (1..10 bits) or is the escape, every emit
-    // entry takes 1..4 codes or is the escape, so the loops over them end
-    // whatever the stream holds.  Tables that break this store nothing.
-    {
-        const uint32_t n_hier = lds_tables * 64u;  // 16-byte pieces
-        constexpr uint32_t kCountPieces = df11i::kCountEntries / 4u, kEmitPieces = df11i::kEmitEntries / 2u;
-        const uint32_t n_all = n_hier + (kMulti ? kCountPieces + kEmitPieces : 0u);
-        const uint4 *hsrc = reinterpret_cast<const uint4 *>(p.tables);
-        const uint4 *msrc = reinterpret_cast<const uint4 *>(p.tables + p.n_tables * 256u);
-        bool bad = false;
-        for (uint32_t i0 = threadIdx.x; i0 < n_all; i0 += 2u * blockDim.x) {
-            uint4 v[2];
-#pragma unroll
-            for (uint32_t k = 0; k < 2; ++k) {
-                const uint32_t i = i0 + k * blockDim.x;
-                if (i < n_all) v[k] = i < n_hier ? hsrc[i] : msrc[i - n_hier];
-            }
-#pragma unroll
-            for (uint32_t k = 0; k < 2; ++k) {
-                const uint32_t i = i0 + k * blockDim.x;
-                if (i >= n_all) continue;
-                if (i < n_hier) {
-                    reinterpret_cast<uint4 *>(lut)[i] = v[k];
-                } else if constexpr (kMulti) {
-                    const uint32_t j = i - n_hier;
-                    if (j < kCountPieces) {
-                        reinterpret_cast<uint4 *>(s_count_table)[j] = v[k];
-                        const uint32_t ce[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-                        for (const uint32_t e : ce) {
-                            const uint32_t t = e & 0xFFu;
-                            bad |= !((t >= 1u && t <= df11i::kCountBits) || e == df11i::kCountEscape);
-                        }
-                    } else {
-                        reinterpret_cast<uint4 *>(s_emit_table)[j - kCountPieces] = v[k];
-                        const uint32_t el[2] = {v[k].x, v[k].z};  // low words of the two entries
-                        for (const uint32_t lo : el) {
-                            const uint32_t m = (lo >> 16) & 127u;
-                            bad |= !((m >= 1u && m <= df11i::kEmitCodes) || m == df11i::kEmitEscape);
-                        }
-                    }
-                }
-            }
-        }
-        if constexpr (kMulti) {
-            if (__syncthreads_or(bad)) return;
-        } else {
-            __syncthreads();
-        }
-    }
-
-    uint16_t *stage = reinterpret_cast<uint16_t *>(lds + lds_tables * 1024u) + wave * p.stage_elems;
-    const uint64_t stride = uniform_u64(uint64_t{gridDim.x} * waves);
-    if (u >= p.n_units) return;  // uniform across the wave
+__device__ __forceinline__ void unit_loop(const KParams &p, const uint32_t *lut, uint16_t *stage, uint32_t lane,
+                                          uint64_t u, uint64_t stride, UnitInputs cur) {
+    const uint64_t last = p.n_units - 1;
     // Wait for the first unit's inputs here: the loop head then sees them
     // complete on both of its entries, and needs no wait that would also
     // drain the previous unit's stores (vmcnt counts loads and stores in
@@ -584,6 +515,87 @@ df11_decode_kernel(KParams p) {
         cur = nxt;  // waits for the next unit's inputs, requested a whole unit ago
         u = un;
     }
+}
+
+template <bool kDeepGlobal, bool kMulti, bool kCounts>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(WavesPerEU<kDeepGlobal>::value)))
+df11_decode_kernel(KParams p) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    // dynamic LDS: hierarchical tables, then one staging area per wave
+    const uint32_t lds_tables = kDeepGlobal ? 1u : p.n_tables;
+    uint32_t *lut = reinterpret_cast<uint32_t *>(lds);
+
+    const uint32_t lane = threadIdx.x & 63u;
+    // wave index and wave count are uniform: keep unit indices in scalar registers
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+    const uint64_t u = uniform_u64(uint64_t{blockIdx.x} * waves + wave);
+    const uint64_t last = p.n_units - 1;  // the host launches only for blocks with weights
+    // The first unit's inputs are requested before the tables are copied, so
+    // that the two memory latencies overlap (a wave with no unit loads the
+    // last one and leaves after the workgroup barrier).
+    UnitInputs cur;
+    load_unit<kCounts>(p, u < last ? u : last, lane, cur);
+    // The tables go to LDS in one pass: every thread requests its 16-byte
+    // pieces (up to two per round) before it stores any, so their latencies
+    // overlap.  The multi-code tables are checked in registers on the way:
+    // every count entry advances (1..10 bits) or is the escape, every emit
+    // entry takes 1..4 codes or is the escape, so the loops over them end
+    // whatever the stream holds.  When any entry breaks this, the workgroup
+    // decodes with the hierarchical tables alone (one code per lookup).
+    bool bad = false;
+    {
+        const uint32_t n_hier = lds_tables * 64u;  // 16-byte pieces
+        constexpr uint32_t kCountPieces = df11i::kCountEntries / 4u, kEmitPieces = df11i::kEmitEntries / 2u;
+        const uint32_t n_all = n_hier + (kMulti ? kCountPieces + kEmitPieces : 0u);
+        const uint4 *hsrc = reinterpret_cast<const uint4 *>(p.tables);
+        const uint4 *msrc = reinterpret_cast<const uint4 *>(p.tables + p.n_tables * 256u);
+        auto fetch = [&](uint32_t i) { return i < n_hier ? hsrc[i] : msrc[i - n_hier]; };
+        auto place = [&](uint32_t i, const uint4 &v) {
+            if (i < n_hier) {
+                reinterpret_cast<uint4 *>(lut)[i] = v;
+            } else if constexpr (kMulti) {
+                const uint32_t j = i - n_hier;
+                if (j < kCountPieces) {
+                    reinterpret_cast<uint4 *>(s_count_table)[j] = v;
+                    const uint32_t ce[4] = {v.x, v.y, v.z, v.w};
+                    for (const uint32_t e : ce) {
+                        const uint32_t t = e & 0xFFu;
+                        bad |= !((t >= 1u && t <= df11i::kCountBits) || e == df11i::kCountEscape);
+                    }
+                } else {
+                    reinterpret_cast<uint4 *>(s_emit_table)[j - kCountPieces] = v;
+                    const uint32_t el[2] = {v.x, v.z};  // low words of the two entries
+                    for (const uint32_t lo : el) {
+                        const uint32_t m = (lo >> 16) & 127u;
+                        bad |= !((m >= 1u && m <= df11i::kEmitCodes) || m == df11i::kEmitEscape);
+                    }
+                }
+            }
+        };
+        for (uint32_t i0 = threadIdx.x; i0 < n_all; i0 += 2u * blockDim.x) {
+            const uint32_t i1 = i0 + blockDim.x;
+            const uint4 v0 = fetch(i0);
+            const uint4 v1 = i1 < n_all ? fetch(i1) : make_uint4(0u, 0u, 0u, 0u);
+            place(i0, v0);
+            if (i1 < n_all) place(i1, v1);
+        }
+        if constexpr (kMulti)
+            bad = __syncthreads_or(bad);
+        else
+            __syncthreads();
+    }
+
+    uint16_t *stage = reinterpret_cast<uint16_t *>(lds + lds_tables * 1024u) + wave * p.stage_elems;
+    const uint64_t stride = uniform_u64(uint64_t{gridDim.x} * waves);
+    if (u >= p.n_units) return;  // uniform across the wave
+    if constexpr (kMulti) {
+        if (__builtin_expect(bad, 0)) {  // uniform across the workgroup
+            unit_loop<kDeepGlobal, false, false>(p, lut, stage, lane, u, stride, cur);
+            return;
+        }
+    }
+    unit_loop<kDeepGlobal, kMulti, kCounts>(p, lut, stage, lane, u, stride, cur);
 }
 
 // ------------------------------------------------------------------ host side

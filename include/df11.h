@@ -256,7 +256,9 @@ df11_status df11_decode_block(const df11_device_block *blk, uint16_t *out_bf16,
  *    DF11_ENCODE_WINDOW_COUNTS), else DF11_E_INVALID_ARG.  Not the pages'
  *    format: a variant that trades one byte per window for the first pass.
  * The multi-code kernels check the count and emit tables when they load them;
- * with entries that no table builder writes, they store nothing. */
+ * a workgroup that finds an entry no table builder writes decodes with the
+ * hierarchical tables alone (as DF11_VARIANT_SINGLE), so the output is still
+ * complete, and exact when the hierarchical tables are intact. */
 #define DF11_VARIANT_SINGLE 1u
 #define DF11_VARIANT_MULTI 2u
 #define DF11_VARIANT_COUNTS 3u
