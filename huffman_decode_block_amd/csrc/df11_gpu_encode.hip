@@ -79,8 +79,11 @@ __global__ void __launch_bounds__(256) hist_zero(uint64_t *hist) {
     if (threadIdx.x < 256) hist[threadIdx.x] = 0;
 }
 
-constexpr uint32_t kHistCopies = 16;  // sub-histograms per workgroup, one per lane & 15
+constexpr uint32_t kHistCopies = 8;   // sub-histograms for exponents outside the window, one per lane & 7
 constexpr uint32_t kHistStride = 257; // padded rows: copies of one exponent fall in different banks
+constexpr uint32_t kWindow = 8;       // exponents counted in lane-private counters per chunk
+constexpr uint32_t kWindowBelow = 5;  // the window starts this many exponents below the last chunk's mode
+constexpr uint32_t kNoWindow = 0x100; // a window base that no exponent reaches (the first chunk)
 
 // Thread t's 16 weights of chunk c as two 16-byte loads (zeros past the
 // block's end, through a buffer range that stops there).
@@ -93,21 +96,46 @@ __device__ __forceinline__ void hist_load(const uint16_t *x, uint64_t n, uint64_
     b = __builtin_amdgcn_raw_buffer_load_b128(r, 32 * t + 16, 0, 0);
 }
 
+// Largest value over the 64 lanes, in every lane (DPP row shifts and row
+// broadcasts, then lane 63's value).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+    uint32_t m = x;
+    m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, m, 0x111, 0xF, 0xF, true)));  // row_shr:1
+    m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, m, 0x112, 0xF, 0xF, true)));  // row_shr:2
+    m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, m, 0x114, 0xF, 0xF, true)));  // row_shr:4
+    m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, m, 0x118, 0xF, 0xF, true)));  // row_shr:8
+    m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, m, 0x142, 0xA, 0xF, false))); // row_bcast:15
+    m = max(m, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0u, m, 0x143, 0xC, 0xF, false))); // row_bcast:31
+    return __builtin_amdgcn_readlane(m, 63);
+}
+
 __global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *x, uint64_t n, uint64_t *hist,
                                                         uint16_t *chunk_hist) {
-    // A block's values cluster on a few exponents: same-address LDS atomics
-    // are serialised, so lanes spread over 16 copies of the histogram.
-    // Thread t owns exponent t: after each chunk it adds up and clears the
-    // copies of its bin, records the chunk's count and keeps a running total.
-    // Each chunk's weights are requested a chunk ahead; the barriers order LDS
-    // only, so the chunk's count store is not waited for.
+    // Weight exponents cluster on a few values, and same-address LDS atomics
+    // are serialised.  So each wave counts a window of 8 exponents, from 5
+    // below the previous chunk's most frequent exponent, in lane-private LDS
+    // counters (counter d of lane l at word 64d + l: no two lanes ever share a
+    // bank or an address), and only exponents outside the window go to
+    // sub-histograms shared by the lanes (8 copies, one per lane & 7).  After
+    // each chunk a wave adds its window counters over its lanes (DPP) into
+    // copy 0; thread t then owns exponent t: it adds up and clears the copies
+    // of its bin, records the chunk's count, keeps a running total and offers
+    // the bin to the choice of the next window.  The first chunk of a
+    // workgroup has no window.  Each chunk's weights are requested a chunk
+    // ahead; the barriers order LDS only, so the chunk's count store is not
+    // waited for.
     __shared__ uint32_t h[kHistCopies * kHistStride];
-    const uint32_t t = threadIdx.x;
+    __shared__ uint32_t win[kThreads / 64][kWindow * 64];
+    __shared__ uint32_t wmax[kThreads / 64];
+    const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
     uint32_t *mine = h + (t & (kHistCopies - 1)) * kHistStride;
+    uint32_t *wc = &win[wave][lane];
     for (uint32_t i = t; i < kHistCopies * kHistStride; i += blockDim.x) h[i] = 0;
+    for (uint32_t d = 0; d < kWindow; ++d) wc[64 * d] = 0;
     __syncthreads();
     const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
     uint64_t total = 0;
+    uint32_t base = kNoWindow;  // uniform
     uint64_t c = blockIdx.x;
     df11w::v4u a, b;
     hist_load(x, n, c, t, a, b);
@@ -118,12 +146,33 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *x, uint6
         if (i0 + kPerThread <= n) {
             const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                atomicAdd(&mine[exponent_of(w[k])], 1u);
-                atomicAdd(&mine[exponent_of(w[k] >> 16)], 1u);
+            for (int k = 0; k < 16; ++k) {
+                const uint32_t e = exponent_of(w[k / 2] >> (16 * (k & 1)));
+                const uint32_t d = e - base;
+                if (d < kWindow)
+                    atomicAdd(wc + 64 * d, 1u);  // this lane's own counter
+                else
+                    atomicAdd(&mine[e], 1u);
             }
         } else {
             for (uint64_t i = i0; i < n && i < i0 + kPerThread; ++i) atomicAdd(&mine[exponent_of(x[i])], 1u);
+        }
+        if (base != kNoWindow) {  // uniform: the wave's window counts, summed over its lanes, into copy 0
+            uint32_t pair[kWindow / 2];
+#pragma unroll
+            for (uint32_t j = 0; j < kWindow / 2; ++j) {  // counts of at most 16 per lane: two per word
+                pair[j] = wc[64 * (2 * j)] | (wc[64 * (2 * j + 1)] << 16);
+                wc[64 * (2 * j)] = 0;
+                wc[64 * (2 * j + 1)] = 0;
+            }
+#pragma unroll
+            for (uint32_t j = 0; j < kWindow / 2; ++j) {
+                const uint32_t sum = __builtin_amdgcn_readlane(df11w::wave_inclusive_scan(pair[j]), 63);
+                if (lane == 0) {
+                    atomicAdd(&h[base + 2 * j], sum & 0xFFFFu);
+                    atomicAdd(&h[base + 2 * j + 1], sum >> 16);
+                }
+            }
         }
         lds_barrier();
         uint32_t cnt = 0;
@@ -134,7 +183,15 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *x, uint6
         }
         if (chunk_hist) chunk_hist[c * 256 + t] = static_cast<uint16_t>(cnt);  // at most 4,096
         total += cnt;
+        // the chunk's most frequent exponent (ties: the larger exponent)
+        const uint32_t top = wave_max((cnt << 8) | t);
+        if (lane == 0) wmax[wave] = top;
         lds_barrier();
+        uint32_t best = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kThreads / 64; ++k) best = max(best, wmax[k]);
+        const uint32_t mode = best & 0xFFu;
+        base = __builtin_amdgcn_readfirstlane(min(mode > kWindowBelow ? mode - kWindowBelow : 0u, 256u - kWindow));
         a = na;
         b = nb;
     }
@@ -345,7 +402,8 @@ __device__ __forceinline__ void pack_chunk(const EncParams &p, uint64_t c, const
         smw[k] = __builtin_amdgcn_perm(sb, sa, 0x06040200u);
     }
     if (kWhole || m == kPackPer) {
-        reinterpret_cast<uint2 *>(p.sm + i0)[0] = make_uint2(smw[0], smw[1]);
+        // written once and not read here: non-temporal (as whole lines per wave)
+        __builtin_nontemporal_store(df11w::v2u{smw[0], smw[1]}, reinterpret_cast<df11w::v2u *>(p.sm + i0));
     } else {
         for (uint32_t k = 0; k < m; ++k) p.sm[i0 + k] = static_cast<uint8_t>(smw[k / 4] >> (8 * (k & 3)));
     }

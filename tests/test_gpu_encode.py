@@ -103,6 +103,45 @@ def test_histogram(torch):
         assert torch.equal(h, h2)
 
 
+def test_histogram_when_the_exponent_mode_moves_between_chunks(torch):
+    """The histogram pass counts a window of exponents around the previous
+    chunk's most frequent one in per-lane counters and the rest with shared
+    atomics: chunks whose distributions jump (small and large scales, one
+    exponent, every exponent, exponents 0 and 255 at the edges of the range),
+    in an order that moves the window up, down and to both ends, give the
+    same counts as numpy, per chunk and in total."""
+    rng = np.random.default_rng(21)
+    parts = []
+    for k, kind in enumerate(["n-2", "n-30", "single255", "all", "n-2", "single0", "t", "n-9", "all", "single128",
+                              "n-2", "n-30"] * 4):
+        if kind.startswith("n"):
+            v = rng.normal(0, 2.0 ** int(kind[1:]), 4096 * (1 + k % 3)).astype(np.float32)
+            parts.append((v.view(np.uint32) >> 16).astype(np.uint16))
+        elif kind.startswith("single"):
+            parts.append(di.single_exponent(4096 * (1 + k % 2), int(kind[6:]), k))
+        elif kind == "all":
+            parts.append(di.all_bf16_patterns(k)[:4096 * 3])
+        else:
+            v = (rng.standard_t(3, 4096) * 1e-3).astype(np.float32)
+            parts.append((v.view(np.uint32) >> 16).astype(np.uint16))
+    x = np.concatenate(parts)
+    x = x[: x.size - 1234]  # a ragged last chunk
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    h = torch.empty(256, dtype=torch.int64, device="cuda")
+    nb = hdb.df11_gpu_chunk_hist_bytes(x.size)
+    ch = torch.full((nb // 2,), -1, dtype=torch.int16, device="cuda")
+    say(f"histogram with moving modes: n={x.size}")
+    hdb.df11_gpu_histogram(xd, h, ch)
+    torch.cuda.synchronize()
+    e = (x >> 7) & 0xFF
+    np.testing.assert_array_equal(h.cpu().numpy(), np.bincount(e, minlength=256))
+    got = ch.cpu().numpy().view(np.uint16).reshape(-1, 256)
+    want = np.stack([np.bincount(e[4096 * c:4096 * (c + 1)], minlength=256) for c in range(got.shape[0])])
+    np.testing.assert_array_equal(got, want)
+    # and the whole encoder on it
+    check(torch, x, "moving modes", counts=True)
+
+
 def test_workload_c2(torch):
     check(torch, di.generate("C2"), "C2", counts=True)
 
