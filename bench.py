@@ -286,7 +286,10 @@ def gpu_encode_bench(args, dev) -> None:
 def overlap_bench(args, dev) -> None:
     """Exposed decode time per block when block i+1 is decoded on a side stream
     while block i's seven GEMMs (torch F.linear, BF16, synthetic activations of
-    `batch` tokens) run: the pages' decompress-just-before-use schedule."""
+    `batch` tokens) run: the pages' decompress-just-before-use schedule.  Also
+    the serial order (each block decoded on the GEMMs' stream right before
+    them) and DecodeAhead's "auto" mode, which times both once per batch size
+    and keeps the faster."""
     import numpy as np
     import torch
     import torch.nn.functional as F
@@ -349,14 +352,28 @@ def overlap_bench(args, dev) -> None:
         # workgroups (it then streams on fewer CUs and leaves the rest to the
         # GEMMs, which matters once they are compute-bound).
         per_launch = {}
+        ahead.mode = "ahead"
         for wv, mg in ((0, 0), (0, 256), (8, 0), (8, 512), (4, 0), (4, 1024), (4, 512), (2, 0)):
             ahead.launch = None if (wv, mg) == (0, 0) else (wv, mg, 0, 0)
             for _ in range(2):
                 ahead.run(consume, stream=stream)
             per_launch[(wv, mg)] = timed(lambda: ahead.run(consume, stream=stream)) / nb
-        ahead.launch = None
         best = min(per_launch, key=per_launch.get)
         t_p = per_launch[best]
+        # the same blocks decoded inline, on the consumer's stream right
+        # before each consumer (the serial order, default launch)
+        ahead.launch = None
+        ahead.mode = "inline"
+        for _ in range(2):
+            ahead.run(consume, stream=stream)
+        t_s = timed(lambda: ahead.run(consume, stream=stream)) / nb
+        # auto: both schedules timed once for this batch (the ahead decode with
+        # the best launch found above), the faster kept, then timed like the others
+        ahead.launch = None if best == (0, 0) else (best[0], best[1], 0, 0)
+        ahead.mode = "auto"
+        picked = ahead.calibrate(consume, stream=stream, key=bs)
+        t_a = timed(lambda: ahead.run(consume, stream=stream, key=bs)) / nb
+        ahead.launch = None
         name = lambda k: f"{k[0] or 'default'} waves/group, " + (f"{k[1]} groups" if k[1] else "default grid")  # noqa: E731
         res = {
             "metric": "exposed decode time per block, next block decoded on a side stream during this block's GEMMs",
@@ -365,6 +382,10 @@ def overlap_bench(args, dev) -> None:
             "gemms_only_us_per_block": round(t_g * 1e6, 2),
             "decode_only_us_per_block": round(t_d * 1e6, 2),
             "pipelined_us_per_block": round(t_p * 1e6, 2),
+            "serial_us_per_block": round(t_s * 1e6, 2),
+            "auto_schedule": picked,
+            "auto_us_per_block": round(t_a * 1e6, 2),
+            "auto_over_serial": round(t_a / t_s, 3),
             "pipelined_over_bf16": round(t_p / t_g, 3),
             "decode_launch": name(best),
             "pipelined_us_by_decode_launch": {name(k): round(v * 1e6, 2) for k, v in per_launch.items()},

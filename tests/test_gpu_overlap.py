@@ -31,14 +31,15 @@ def _blocks(torch, n_blocks):
     return blocks, originals
 
 
+@pytest.mark.parametrize("mode", ["ahead", "inline"])
 @pytest.mark.parametrize("order", [[0, 1, 2], [0, 1, 2, 0, 1, 2], [2], [1, 1, 0]])
-def test_decode_ahead_feeds_exact_weights(torch, order):
+def test_decode_ahead_feeds_exact_weights(torch, order, mode):
     import torch.nn.functional as F
-    print(f"[gpu-test] decode-ahead order={order}", flush=True)
+    print(f"[gpu-test] decode-ahead order={order} mode={mode}", flush=True)
     blocks, originals = _blocks(torch, 3)
     gen = torch.Generator(device="cuda").manual_seed(7)
     xs = {c: torch.randn(64, c, device="cuda", generator=gen).to(torch.bfloat16) for c in (512, 1024)}
-    ahead = DecodeAhead(blocks, [SHAPES] * 3)
+    ahead = DecodeAhead(blocks, [SHAPES] * 3, mode=mode)
     stream = torch.cuda.current_stream()
     seen, outs = [], []
 
@@ -78,6 +79,37 @@ def test_consecutive_runs_do_not_overwrite_a_buffer_still_in_use(torch):
     ahead.run(quick, stream=stream, order=[2, 2, 1])
     torch.cuda.synchronize()
     assert [i for i, _ in seen] == [0, 1, 2, 2, 1]
+    for i, ws in seen:
+        for w, ref in zip(ws, originals[i]):
+            assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), f"block {i} weights differ"
+
+
+def test_auto_mode_picks_a_schedule_per_key_and_mixed_runs_stay_exact(torch):
+    """"auto" times both schedules for a new key (calling the consumer), keeps
+    the faster, and later runs with that key use it; runs in different
+    schedules on the same buffers, back to back, still feed exact weights."""
+    print("[gpu-test] decode-ahead: auto mode", flush=True)
+    blocks, originals = _blocks(torch, 3)
+    ahead = DecodeAhead(blocks, [SHAPES] * 3, mode="auto")
+    stream = torch.cuda.current_stream()
+    seen = []
+
+    def record(i, views):
+        seen.append((i, [v.clone() for v in views]))
+
+    used = ahead.run(record, stream=stream, order=[0, 1, 2], key="k")
+    assert used in ("ahead", "inline") and ahead.choice["k"] == used
+    assert set(ahead.timings["k"]) == {"ahead", "inline"}
+    calls = len(seen)
+    assert calls == 3 * (1 + 4) * 2 + 3  # untimed + 4 timed runs per schedule, then the run itself
+    assert ahead.run(record, stream=stream, order=[2, 0], key="k") == used
+    assert len(seen) == calls + 2
+    # explicit schedules alternating on the same buffers
+    ahead.mode = "inline"
+    ahead.run(record, stream=stream, order=[1, 2])
+    ahead.mode = "ahead"
+    ahead.run(record, stream=stream, order=[0, 1, 2])
+    torch.cuda.synchronize()
     for i, ws in seen:
         for w, ref in zip(ws, originals[i]):
             assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), f"block {i} weights differ"
