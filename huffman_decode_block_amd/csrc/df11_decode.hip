@@ -213,19 +213,25 @@ struct Look96 {
 };
 
 // Up to four codes per lookup.  Each step writes the entry's four 16-bit
-// slots at the lane's next slot with four 2-byte LDS stores: the slots past
-// the entry's n codes are rewritten by the lane's next step, so only the
-// lane's own range is ever written and the staging needs no clearing.  The
-// stores are volatile so that they stay 2-byte stores: merged into one
-// 8-byte store at a 2-byte aligned address they would stall the LDS pipe.
-// Slots carry control fields in bits 6..0, below the exponent, which the
-// merge never reads.  An escape entry (first code longer than the index)
-// shifts by 0 and moves the lane's cursor 64 slots on, which ends the loop
-// with no test in its body; the lane then undoes that, takes the code from
-// the hierarchical tables and goes back in (the slots the escape entry wrote
-// lie inside the lane's range and are rewritten).  The last one to three
-// codes are written one slot at a time, only as many as the lane owns.
+// slots at the lane's next slot q with two LDS stores: slot 0 as a 2-byte
+// store, then one dword pair at the first 4-byte boundary at or after q,
+// which holds slots 0..3 when q is even and slots 1..3 plus one spare slot
+// when q is odd.  The slots past the entry's n codes (and the spare) are
+// rewritten by the lane's next step, so only the lane's own range is ever
+// written and the staging needs no clearing; this needs q + 4 inside the
+// range, so full steps run while at least five slots are left.  (A single
+// 8-byte store at a 2-byte aligned address would stall the LDS pipe, and four
+// 2-byte stores cost twice the LDS issue of these two.)  Slots carry control
+// fields in bits 6..0, below the exponent, which the merge never reads.  An
+// escape entry (first code longer than the index) shifts by 0 and moves the
+// lane's cursor 64 slots on, which ends the loop with no test in its body;
+// the lane then undoes that, takes the code from the hierarchical tables and
+// goes back in (the slots the escape entry wrote lie inside the lane's range
+// and are rewritten).  The last one to four codes are written one slot at a
+// time, only as many as the lane owns.
 typedef __attribute__((address_space(3))) volatile uint16_t lds_u16;
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef __attribute__((address_space(3))) u32x2_a4 lds_pair;
 
 __device__ __forceinline__ lds_u16 *lds_slot(uint32_t b) { return reinterpret_cast<lds_u16 *>(b); }
 
@@ -235,7 +241,7 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
     // the staging is LDS: the low 32 bits of its generic address are the LDS address
     uint32_t b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage)) + 2u * first;
     const uint32_t bend = b + 2u * n;  // past the lane's last slot
-    const uint32_t bfull = bend - 2u * df11i::kEmitCodes;  // last start with four own slots (LDS addresses are far above 8)
+    const uint32_t bfull = bend - 2u * (df11i::kEmitCodes + 1u);  // last start with five own slots (LDS addresses are far above 10)
     auto entry = [&]() { return *reinterpret_cast<const uint64_t *>(et + (s.h() >> (32 - df11i::kEmitBits))); };
     auto escape_step = [&]() {
         const uint32_t e = lookup<kDeepGlobal>(lut, p.tables, p.n_tables, s.h());
@@ -253,11 +259,13 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
         while (b <= bfull) {
             const uint32_t lo = static_cast<uint32_t>(ev), hi = static_cast<uint32_t>(ev >> 32);
             s.shift(lo);
-            lds_u16 *w = lds_slot(b);
-            w[0] = static_cast<uint16_t>(lo);
-            w[1] = static_cast<uint16_t>(lo >> 16);
-            w[2] = static_cast<uint16_t>(hi);
-            w[3] = static_cast<uint16_t>(hi >> 16);
+            *lds_slot(b) = static_cast<uint16_t>(lo);
+            const uint32_t odd = b & 2u;  // q odd: the pair starts one slot on
+            const uint32_t sh = odd << 3;
+            u32x2_a4 pair;
+            pair.x = __builtin_amdgcn_alignbit(hi, lo, sh);
+            pair.y = hi >> sh;
+            *reinterpret_cast<lds_pair *>(b + odd) = pair;
             // n slots, or 64 for an escape; the field is kept opaque so that
             // the advance is one bitfield extract and one shift-add
             uint32_t nslots = __builtin_amdgcn_ubfe(lo, 16u, 7u);
@@ -269,7 +277,7 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
         b -= 2u * df11i::kEmitEscape;
         escape_step();
     }
-    while (b < bend) {  // the last one to three codes
+    while (b < bend) {  // the last one to four codes
         const uint64_t ev = entry();
         const uint32_t lo = static_cast<uint32_t>(ev);
         const uint32_t m = (lo >> 16) & 127u;
@@ -277,12 +285,13 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
             escape_step();
             continue;
         }
-        const uint32_t left = (bend - b) >> 1;  // 1..3
+        const uint32_t left = (bend - b) >> 1;  // 1..4
         const uint32_t k = m < left ? m : left;
         lds_u16 *w = lds_slot(b);
         w[0] = static_cast<uint16_t>(lo);
         if (k > 1) w[1] = static_cast<uint16_t>(lo >> 16);
         if (k > 2) w[2] = static_cast<uint16_t>(ev >> 32);
+        if (k > 3) w[3] = static_cast<uint16_t>(ev >> 48);
         b += 2u * k;
         s.shift(lo);  // past the lane's last code the state is not used
     }
