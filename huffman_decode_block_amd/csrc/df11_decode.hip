@@ -302,6 +302,10 @@ __device__ __forceinline__ void emit_multi(const uint32_t *lut, const uint2 *et,
 // kernels reference them, so only those allocate them.
 __shared__ __align__(16) uint32_t s_count_table[df11i::kCountEntries];
 __shared__ __align__(16) uint2 s_emit_table[df11i::kEmitEntries];
+// one word per wave: whether that wave found a bad multi-code table entry
+constexpr uint32_t kMaxWaves = 16;
+__shared__ __align__(16) uint32_t s_wave_bad[kMaxWaves];
+constexpr uint32_t kMultiStaticBytes = static_cast<uint32_t>(df11i::kMultiTableBytes) + 4u * kMaxWaves;
 
 using df11w::kNonTemporal;
 using df11w::kOff;
@@ -545,21 +549,27 @@ df11_decode_kernel(KParams p) {
     // last one and leaves after the workgroup barrier).
     UnitInputs cur;
     load_unit<kCounts>(p, u < last ? u : last, lane, cur);
-    // The tables go to LDS in one pass: every thread requests its 16-byte
-    // pieces (up to two per round) before it stores any, so their latencies
-    // overlap.  The multi-code tables are checked in registers on the way:
-    // every count entry advances (1..10 bits) or is the escape, every emit
-    // entry takes 1..4 codes or is the escape, so the loops over them end
-    // whatever the stream holds.  When any entry breaks this, the workgroup
-    // decodes with the hierarchical tables alone (one code per lookup).
+    // The tables go to LDS in one pass.  Every thread requests its first two
+    // 16-byte pieces in straight-line code, right after the unit's inputs and
+    // before it waits for anything, so the two memory latencies overlap (a
+    // loop here would wait for every earlier load at its head); more pieces
+    // per thread (small workgroups, many sub-tables) go in a loop after that.
+    // The multi-code tables are checked in registers on the way: every count
+    // entry advances (1..10 bits) or is the escape, every emit entry takes
+    // 1..4 codes or is the escape, so the loops over them end whatever the
+    // stream holds.  When any entry breaks this, the workgroup decodes with
+    // the hierarchical tables alone (one code per lookup).  Each wave leaves
+    // its verdict in its own LDS word, read by all after the one barrier.
     bool bad = false;
     {
         const uint32_t n_hier = lds_tables * 64u;  // 16-byte pieces
         constexpr uint32_t kCountPieces = df11i::kCountEntries / 4u, kEmitPieces = df11i::kEmitEntries / 2u;
         const uint32_t n_all = n_hier + (kMulti ? kCountPieces + kEmitPieces : 0u);
-        const uint4 *hsrc = reinterpret_cast<const uint4 *>(p.tables);
-        const uint4 *msrc = reinterpret_cast<const uint4 *>(p.tables + p.n_tables * 256u);
-        auto fetch = [&](uint32_t i) { return i < n_hier ? hsrc[i] : msrc[i - n_hier]; };
+        // piece i < n_hier is hierarchical piece i; the multi-code tables
+        // follow all n_tables hierarchical tables in the blob
+        const uint32_t skip = (p.n_tables - lds_tables) * 64u;
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.tables);
+        auto fetch = [&](uint32_t i) { return src[i + (i < n_hier ? 0u : skip)]; };
         auto place = [&](uint32_t i, const uint4 &v) {
             if (i < n_hier) {
                 reinterpret_cast<uint4 *>(lut)[i] = v;
@@ -582,17 +592,23 @@ df11_decode_kernel(KParams p) {
                 }
             }
         };
-        for (uint32_t i0 = threadIdx.x; i0 < n_all; i0 += 2u * blockDim.x) {
-            const uint32_t i1 = i0 + blockDim.x;
-            const uint4 v0 = fetch(i0);
-            const uint4 v1 = i1 < n_all ? fetch(i1) : make_uint4(0u, 0u, 0u, 0u);
-            place(i0, v0);
-            if (i1 < n_all) place(i1, v1);
+        const uint32_t nthr = blockDim.x;
+        const uint32_t i0 = threadIdx.x, i1 = i0 + nthr;
+        const uint4 v0 = fetch(min(i0, n_all - 1u));  // clamped: always a piece of the tables
+        const uint4 v1 = fetch(min(i1, n_all - 1u));
+        if (i0 < n_all) place(i0, v0);
+        if (i1 < n_all) place(i1, v1);
+        for (uint32_t i = i1 + nthr; i < n_all; i += nthr) place(i, fetch(i));
+        if constexpr (kMulti) {
+            const uint64_t any = __builtin_amdgcn_ballot_w64(bad);
+            if (lane == 0) s_wave_bad[wave] = any != 0 ? 1u : 0u;
         }
-        if constexpr (kMulti)
-            bad = __syncthreads_or(bad);
-        else
-            __syncthreads();
+        __syncthreads();
+        if constexpr (kMulti) {
+            uint32_t f = 0;
+            for (uint32_t w = 0; w < waves; ++w) f |= s_wave_bad[w];
+            bad = f != 0;
+        }
     }
 
     uint16_t *stage = reinterpret_cast<uint16_t *>(lds + lds_tables * 1024u) + wave * p.stage_elems;
@@ -721,7 +737,7 @@ df11_status decode_block(const df11_device_block *blk, uint16_t *out_bf16, uint6
     // LDS per workgroup: static (count and emit tables) + hierarchical tables
     // + one staging area per wave; it bounds how many waves are resident.
     const uint32_t lds_tables = deep_global ? 1u : blk->n_tables;
-    const uint32_t fixed_static = multi ? static_cast<uint32_t>(df11i::kMultiTableBytes) : 0u;
+    const uint32_t fixed_static = multi ? kMultiStaticBytes : 0u;
     // staging: the unit's outputs after up to 7 slots of lead, rounded to
     // 8-output chunks
     const uint32_t stage_elems = static_cast<uint32_t>((blk->max_unit_count + 7 + 7) / 8 * 8);
