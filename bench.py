@@ -7,8 +7,10 @@ weights, one shared codebook), inputs resident in HBM, with the caches
 flushed before it: a read of 1 GiB of unrelated data pushes the block out of
 the L2s and the 256 MB Infinity Cache, as a model's other work does between
 two block decodes.  Flush and decode pairs are enqueued back to back with no
-host synchronisation; each decode is timed by its own HIP event pair.  The
-launches rotate over device copies of the block.  Prints one JSON line.
+host synchronisation; each decode is timed with HIP events as the difference
+of (flush, decode) and (flush) each between one event pair (an event recorded
+between the two kernels would delay the decode's start; see ColdSchedule).
+The launches rotate over device copies of the block.  Prints one JSON line.
 
   value      decoded BF16 GB/s = 2 * weights / mean decode time
   roofline   algorithmic HBM bytes per launch (compressed sections read +
@@ -104,9 +106,19 @@ class ColdSchedule:
     unrelated data (an int64 sum, which torch runs on its input as it is; a
     write would leave dirty lines whose write-back competes with the step)
     pushes everything out of the L2s and the 256 MB Infinity Cache, then the
-    launch runs between its own pair of HIP events on the same stream.  Pairs
-    are enqueued back to back with no host synchronisation, so the GPU never
-    idles and its clocks stay up; one synchronize at the end."""
+    launch runs.
+
+    A HIP event recorded between two kernels delays the second kernel's start
+    by ~5.6 us (kernel traces: no gap from the flush to the launch without an
+    event between them, 5.6 us with one), so an event pair around each launch
+    would time that delay too.  Instead each step is timed twice, both times
+    with the event pair outside the kernels: leg A records (event, flush,
+    launch, event), leg B (event, flush, event, launch).  Both intervals hold
+    the same marker delay and a flush that follows a launch; the launch's
+    duration is A - B (per launch: A_i minus B's mean), which the kernel trace
+    of the same command confirms to within 0.2 %.  Steps are enqueued back to
+    back with no host synchronisation, so the GPU never idles and its clocks
+    stay up; one synchronize at the end of each leg."""
 
     FLUSH_BYTES = 1 << 30
 
@@ -115,18 +127,29 @@ class ColdSchedule:
         self.torch = torch
         self.stream = stream
         self.scratch = torch.ones(self.FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+        self.flush_s = None  # leg B's mean of the last run (flush only), seconds
 
-    def run(self, launch, k: int) -> list:
-        """k steps of launch(i); returns each launch's duration in seconds."""
+    def _leg(self, launch, k: int, start: int, inside: bool) -> list:
         torch = self.torch
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
         for i in range(k):
-            self.scratch.sum()
             ev[i][0].record(self.stream)
-            launch(i)
+            self.scratch.sum()
+            if inside:
+                launch(start + i)
             ev[i][1].record(self.stream)
+            if not inside:
+                launch(start + i)
         torch.cuda.synchronize()
         return [a.elapsed_time(b) * 1e-3 for a, b in ev]
+
+    def run(self, launch, k: int) -> list:
+        """k cold steps of launch(i) (and k more for leg B, i = k .. 2k-1);
+        returns each leg-A launch's duration in seconds, A_i - mean(B)."""
+        a = self._leg(launch, k, 0, True)
+        b = self._leg(launch, k, k, False)
+        self.flush_s = sum(b) / len(b)
+        return [t - self.flush_s for t in a]
 
 
 def back_to_back(launch, k: int, stream, start: int = 0) -> float:
@@ -384,6 +407,7 @@ def overlap_bench(args, dev) -> None:
             "pipelined_us_per_block": round(t_p * 1e6, 2),
             "serial_us_per_block": round(t_s * 1e6, 2),
             "auto_schedule": picked,
+            "auto_calibration_us_per_block": {k: round(v / nb * 1e6, 2) for k, v in ahead.timings[bs].items()},
             "auto_us_per_block": round(t_a * 1e6, 2),
             "auto_over_serial": round(t_a / t_s, 3),
             "pipelined_over_bf16": round(t_p / t_g, 3),
@@ -534,7 +558,7 @@ def main():
         """k timed launches of kernel `name` in `schedule`: per-launch times
         (cold) or the region average (rotated), in seconds."""
         fn, start = kernels[name], pos[0]
-        pos[0] += k
+        pos[0] += 2 * k
         if schedule == "cold":
             return cold.run(lambda j: fn(start + j), k)
         return [back_to_back(fn, k, stream, start)]
@@ -633,8 +657,9 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "step": ("one launch over the whole block with the caches flushed before it (a 1 GiB read); value and "
-                 "ms_per_step from the launch's own HIP event pair, the flushes outside (wall_ms_per_step "
-                 "includes them)") if args.schedule == "cold" else
+                 "ms_per_step from HIP events: (flush, launch) timed between one event pair, minus (flush) timed "
+                 "the same way with the launch after its pair, so that the flush and the event marker's dispatch "
+                 "delay cancel (wall_ms_per_step: both legs, flushes included)") if args.schedule == "cold" else
                 ("one launch over the whole block, launches back to back over device copies of the block; "
                  "value and ms_per_step from one HIP event pair around the timed launches"),
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),

@@ -142,6 +142,47 @@ def test_histogram_when_the_exponent_mode_moves_between_chunks(torch):
     check(torch, x, "moving modes", counts=True)
 
 
+def test_histogram_window_follows_each_workgroups_chunks(torch):
+    """With more chunks than histogram workgroups (2,048), each workgroup
+    counts several chunks in turn and places each chunk's window from the
+    one before: here the scale changes every 2,048 chunks, so the chunks of
+    one workgroup jump between scales, one exponent (0, 127, 255), every
+    pattern and heavy tails, and the windows move up, down, to both ends and
+    miss most weights; counts per chunk and in total must still equal
+    numpy's."""
+    rng = np.random.default_rng(33)
+    groups, chunk = 2048, 4096
+    kinds = ["n-2", "n-30", "single255", "all", "n-9", "single0", "t", "n-2", "single127", "n-5"]
+    parts = []
+    for r, kind in enumerate(kinds):  # chunks r * 2048 .. r * 2048 + 2047
+        m = groups * chunk
+        if kind.startswith("n"):
+            v = rng.normal(0, 2.0 ** int(kind[1:]), m).astype(np.float32)
+            parts.append((v.view(np.uint32) >> 16).astype(np.uint16))
+        elif kind.startswith("single"):
+            parts.append(di.single_exponent(m, int(kind[6:]), r))
+        elif kind == "all":
+            parts.append(np.tile(di.all_bf16_patterns(r), m // 65536))
+        else:
+            v = (rng.standard_t(2, m) * 1e-2).astype(np.float32)
+            parts.append((v.view(np.uint32) >> 16).astype(np.uint16))
+    x = np.concatenate(parts)
+    x = x[: x.size - 777]  # a ragged last chunk
+    n_chunks = (x.size + chunk - 1) // chunk
+    assert n_chunks > 4 * groups
+    xd = torch.from_numpy(x.view(np.int16)).to("cuda")
+    h = torch.empty(256, dtype=torch.int64, device="cuda")
+    ch = torch.full((hdb.df11_gpu_chunk_hist_bytes(x.size) // 2,), -1, dtype=torch.int16, device="cuda")
+    say(f"histogram, several chunks per workgroup: n={x.size}")
+    hdb.df11_gpu_histogram(xd, h, ch)
+    torch.cuda.synchronize()
+    e = ((x >> 7) & 0xFF).astype(np.int64)
+    np.testing.assert_array_equal(h.cpu().numpy(), np.bincount(e, minlength=256))
+    want = np.bincount(np.arange(x.size) // chunk * 256 + e, minlength=n_chunks * 256).reshape(n_chunks, 256)
+    got = ch.cpu().numpy().view(np.uint16).reshape(-1, 256)
+    np.testing.assert_array_equal(got, want)
+
+
 def test_workload_c2(torch):
     check(torch, di.generate("C2"), "C2", counts=True)
 

@@ -101,7 +101,7 @@ def test_auto_mode_picks_a_schedule_per_key_and_mixed_runs_stay_exact(torch):
     assert used in ("ahead", "inline") and ahead.choice["k"] == used
     assert set(ahead.timings["k"]) == {"ahead", "inline"}
     calls = len(seen)
-    assert calls == 3 * (1 + 4) * 2 + 3  # untimed + 4 timed runs per schedule, then the run itself
+    assert calls == 3 * (1 + 5) * 2 + 3  # untimed + 5 timed runs per schedule, then the run itself
     assert ahead.run(record, stream=stream, order=[2, 0], key="k") == used
     assert len(seen) == calls + 2
     # explicit schedules alternating on the same buffers
