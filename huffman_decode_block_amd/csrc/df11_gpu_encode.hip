@@ -292,26 +292,44 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *ws
 // One thread per chunk: its bits are the sum over exponents of count x code
 // length; then the exclusive prefix within the segment (one workgroup).
 __global__ void __launch_bounds__(kThreads) bits_kernel(EncParams p) {
+    // The bits of each chunk of this segment from its 256 counts: 8 lanes per
+    // chunk, each reading 32 counts (64 contiguous bytes, so that a wave reads
+    // 8 chunks' counts in one piece), summed over the 8 lanes with DPP; then
+    // the block scan of the segment's 256 chunk totals.
     __shared__ uint32_t len[256];
+    __shared__ uint32_t cbits[kSegChunks];
     __shared__ uint32_t wsum[kThreads / 64];
     const uint32_t t = threadIdx.x;
     len[t] = p.len[t];
     __syncthreads();
-    const uint64_t c = uint64_t{blockIdx.x} * kSegChunks + t;
-    uint32_t bits = 0;
-    if (c < p.n_chunks) {
-        const uint4 *h = reinterpret_cast<const uint4 *>(p.chunk_hist + c * 256);
-#pragma unroll 8
-        for (uint32_t j = 0; j < 32; ++j) {  // exponents 8j .. 8j + 7
-            const uint4 v = h[j];
-            const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t sub = t & 7u;  // this lane's eighth of a chunk's counts
+    const uint64_t seg0 = uint64_t{blockIdx.x} * kSegChunks;
+    for (uint32_t k = t >> 3; k < kSegChunks; k += kThreads / 8) {
+        const uint64_t c = seg0 + k;
+        uint32_t bits = 0;
+        if (c < p.n_chunks) {
+            const uint4 *h = reinterpret_cast<const uint4 *>(p.chunk_hist + c * 256 + 32 * sub);
 #pragma unroll
-            for (uint32_t k = 0; k < 4; ++k)
-                bits += (q[k] & 0xFFFFu) * len[8 * j + 2 * k] + (q[k] >> 16) * len[8 * j + 2 * k + 1];
+            for (uint32_t j = 0; j < 4; ++j) {  // exponents 32 sub + 8j .. 32 sub + 8j + 7
+                const uint4 v = h[j];
+                const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (uint32_t m = 0; m < 4; ++m) {
+                    const uint32_t e = 32 * sub + 8 * j + 2 * m;
+                    bits += (q[m] & 0xFFFFu) * len[e] + (q[m] >> 16) * len[e + 1];
+                }
+            }
         }
+        // sum over the chunk's 8 lanes: quad xor 1, quad xor 2, then half-row mirror
+        bits += __builtin_amdgcn_update_dpp(0u, bits, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+        bits += __builtin_amdgcn_update_dpp(0u, bits, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+        bits += __builtin_amdgcn_update_dpp(0u, bits, 0x141, 0xF, 0xF, false);  // row_half_mirror
+        if (sub == 0) cbits[k] = bits;
     }
+    __syncthreads();
+    const uint64_t c = seg0 + t;
     uint32_t seg_bits;
-    const uint32_t pre = block_exclusive_sum<kThreads / 64>(bits, wsum, seg_bits);
+    const uint32_t pre = block_exclusive_sum<kThreads / 64>(cbits[t], wsum, seg_bits);
     if (c < p.n_chunks) p.chunk_pre[c] = pre;
     if (t == 0) p.seg_sum[blockIdx.x] = seg_bits;
 }
@@ -558,14 +576,46 @@ __global__ void __launch_bounds__(kPackThreads) pack_kernel(EncParams p) {
 __global__ void __launch_bounds__(kThreads) finish_kernel(EncParams p) {
     const uint64_t tid = uint64_t{blockIdx.x} * blockDim.x + threadIdx.x;
     const uint64_t step = uint64_t{gridDim.x} * blockDim.x;
+    // 5-bit gap fields, 8 windows per 5 bytes (big-endian), 32 windows per
+    // thread: the gap bytes read as four 8-byte words, the 20 field bytes
+    // written as five 4-byte words (byte by byte at the end of the section or
+    // when the section is not 4-byte aligned).
     const uint64_t groups = (p.n_windows + 7) / 8;
-    for (uint64_t g = tid; g < groups; g += step) {
-        uint64_t v = 0;
-        for (uint32_t j = 0; j < 8; ++j) {
-            const uint64_t w = 8 * g + j;
-            v = (v << 5) | (w < p.n_windows ? (p.gap8[w] & 31u) : 0u);
+    const uint64_t quads = (groups + 3) / 4;
+    const bool words = (reinterpret_cast<uintptr_t>(p.gaps) & 3u) == 0;
+    for (uint64_t q = tid; q < quads; q += step) {
+        const uint64_t w0 = 32 * q;
+        uint64_t g[4] = {0, 0, 0, 0};  // window w0 + 8i + j in byte j of g[i]
+        if (w0 + 32 <= p.n_windows) {
+            const uint64_t *src = reinterpret_cast<const uint64_t *>(p.gap8 + w0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g[i] = src[i];
+        } else {
+            for (uint32_t j = 0; j < 32 && w0 + j < p.n_windows; ++j)
+                g[j / 8] |= static_cast<uint64_t>(p.gap8[w0 + j]) << (8 * (j % 8));
         }
-        for (uint32_t k = 0; k < 5; ++k) p.gaps[5 * g + k] = static_cast<uint8_t>(v >> (32 - 8 * k));
+        uint64_t v[4];  // each group's 40 field bits
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[i] = (v[i] << 5) | ((g[i] >> (8 * j)) & 31u);
+        }
+        const uint32_t wd[5] = {  // the 160 field bits as big-endian words
+            static_cast<uint32_t>(v[0] >> 8),
+            static_cast<uint32_t>((v[0] << 24) | (v[1] >> 16)),
+            static_cast<uint32_t>((v[1] << 16) | (v[2] >> 24)),
+            static_cast<uint32_t>((v[2] << 8) | (v[3] >> 32)),
+            static_cast<uint32_t>(v[3])};
+        const uint64_t b0 = 20 * q;
+        if (words && b0 + 20 <= p.gaps_bytes) {
+            uint32_t *dst = reinterpret_cast<uint32_t *>(p.gaps + b0);
+#pragma unroll
+            for (int k = 0; k < 5; ++k) dst[k] = __builtin_bswap32(wd[k]);
+        } else {
+            for (uint32_t k = 0; k < 20 && b0 + k < p.gaps_bytes; ++k)
+                p.gaps[b0 + k] = static_cast<uint8_t>(wd[k / 4] >> (24 - 8 * (k % 4)));
+        }
     }
     if (p.counts)
         for (uint64_t w = tid; w < p.n_windows; w += step)
@@ -783,7 +833,8 @@ df11_status gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint1
         // taking many chunks so that the next chunk's loads overlap the current
         err = launch(pack_kernel, std::min<uint32_t>(chunks, pack_groups()), kPackThreads, st, p);
     }
-    if (err == hipSuccess && nw) err = launch(finish_kernel, grid_for(nw / 8 + 1, 4096), kThreads, st, p);
+    if (err == hipSuccess && nw)
+        err = launch(finish_kernel, grid_for(with_counts ? nw : nw / 32 + 1, 4096), kThreads, st, p);
     if (err != hipSuccess) {
         df11i::last_hip_error = static_cast<int32_t>(err);
         return DF11_E_HIP;
