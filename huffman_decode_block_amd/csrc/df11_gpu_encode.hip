@@ -12,14 +12,14 @@
 // Passes (one stream, in order):
 //   hist    (df11_gpu_histogram) per chunk of 4,096 weights its 256 exponent
 //           counts, and their sum over the block
-//   fill    the padding past what later passes write (stream, gaps, counts,
-//           sign/mantissa); unit_pos and the first-start records preset for
-//           the last unit and window, the only ones where no code may start
 //   bits    bits per chunk from its counts and the code lengths (the weights
 //           are not read again), and their exclusive prefix within each
 //           segment of 256 chunks
 //   top     exclusive prefix of the segment totals (one workgroup)
-//   bounds  zeroes the stream words that two neighbouring chunks share
+//   bounds  zeroes the stream words that two neighbouring chunks share and
+//           the padding past what later passes write (stream, gaps, counts,
+//           sign/mantissa); presets unit_pos and the first-start records for
+//           the last unit and window, the only ones where no code may start
 //   pack    persistent, per chunk: each weight's bit offset (block scan),
 //           its sign/mantissa byte, its code and its start ORed into an LDS
 //           bit buffer and an LDS start bitmap; the buffer is written out
@@ -199,14 +199,11 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *x, uint6
     if (total) atomicAdd(reinterpret_cast<unsigned long long *>(hist + t), static_cast<unsigned long long>(total));
 }
 
-// ---------------------------------------------------------------- fill
-__global__ void __launch_bounds__(kThreads) fill_kernel(EncParams p) {
+// ---------------------------------------------------------------- padding
+__device__ __forceinline__ void fill_padding(const EncParams &p, uint64_t tid, uint64_t step) {
     // Only what no later pass writes: pack stores every stream word up to the
     // one holding the last code bit, finish every gap byte of the 5-byte groups
-    // and every window count, so only the padding past them is zeroed here (the
-    // words that two chunks share are zeroed by bounds_kernel).
-    const uint64_t tid = uint64_t{blockIdx.x} * blockDim.x + threadIdx.x;
-    const uint64_t step = uint64_t{gridDim.x} * blockDim.x;
+    // and every window count, so only the padding past them is zeroed here.
     for (uint64_t i = p.total_bits / 32 * 4 + tid; i < p.stream_bytes; i += step) p.stream[i] = 0;
     for (uint64_t i = (p.n_windows + 7) / 8 * 5 + tid; i < p.gaps_bytes; i += step) p.gaps[i] = 0;
     for (uint64_t i = p.n + tid; i < p.sm_bytes; i += step) p.sm[i] = 0;
@@ -225,16 +222,6 @@ __global__ void __launch_bounds__(kThreads) fill_kernel(EncParams p) {
             p.wfirst[p.n_windows] = p.n;
         }
     }
-}
-
-// Zeroes the stream word where chunk c starts when the previous chunk ends
-// inside it: both chunks OR their bits into that word (after the two prefix
-// passes, before pack).
-__global__ void __launch_bounds__(kThreads) bounds_kernel(EncParams p) {
-    const uint64_t c = uint64_t{blockIdx.x} * blockDim.x + threadIdx.x;
-    if (c == 0 || c >= p.n_chunks) return;
-    const uint64_t cb = p.seg_off[c / kSegChunks] + p.chunk_pre[c];
-    if (cb & 31u) reinterpret_cast<uint32_t *>(p.stream)[cb >> 5] = 0;
 }
 
 // Weights of pack thread t of chunk c, eight as four packed words (two
@@ -358,6 +345,20 @@ __global__ void __launch_bounds__(kScanThreads) top_kernel(EncParams p) {
         run += p.seg_sum[k];
     }
     if (t == kScanThreads - 1) p.seg_off[p.n_segs] = part[t];
+}
+
+// Before pack, with every chunk's first bit known: the stream word where
+// chunk c starts is shared with the previous chunk when that one ends inside
+// it (both OR their bits into it), so it is zeroed; and the padding and
+// presets of fill_padding.
+__global__ void __launch_bounds__(kThreads) bounds_kernel(EncParams p) {
+    const uint64_t tid = uint64_t{blockIdx.x} * blockDim.x + threadIdx.x;
+    const uint64_t step = uint64_t{gridDim.x} * blockDim.x;
+    for (uint64_t c = 1 + tid; c < p.n_chunks; c += step) {
+        const uint64_t cb = p.seg_off[c / kSegChunks] + p.chunk_pre[c];
+        if (cb & 31u) reinterpret_cast<uint32_t *>(p.stream)[cb >> 5] = 0;
+    }
+    fill_padding(p, tid, step);
 }
 
 // ---------------------------------------------------------------- pack
@@ -823,11 +824,10 @@ df11_status gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint1
 
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const uint32_t chunks = static_cast<uint32_t>(p.n_chunks);
-    hipError_t err = launch(fill_kernel, 1, kThreads, st, p);
-    if (err == hipSuccess && chunks)
-        err = launch(bits_kernel, static_cast<uint32_t>(p.n_segs), kThreads, st, p);
+    hipError_t err = hipSuccess;
+    if (chunks) err = launch(bits_kernel, static_cast<uint32_t>(p.n_segs), kThreads, st, p);
     if (err == hipSuccess && chunks) err = launch(top_kernel, 1, kScanThreads, st, p);
-    if (err == hipSuccess && chunks) err = launch(bounds_kernel, grid_for(p.n_chunks, 1u << 20), kThreads, st, p);
+    if (err == hipSuccess) err = launch(bounds_kernel, grid_for(p.n_chunks, 1u << 20), kThreads, st, p);
     if (err == hipSuccess && chunks) {
         // a few workgroups per resident slot: enough to fill the GPU, each
         // taking many chunks so that the next chunk's loads overlap the current
