@@ -80,21 +80,28 @@ __global__ void __launch_bounds__(256) hist_zero(uint64_t *hist) {
     if (threadIdx.x < 256) hist[threadIdx.x] = 0;
 }
 
-constexpr uint32_t kHistCopies = 8;   // sub-histograms for exponents outside the window, one per lane & 7
-constexpr uint32_t kHistStride = 257; // padded rows: copies of one exponent fall in different banks
-constexpr uint32_t kWindow = 8;       // exponents counted in lane-private counters per chunk
-constexpr uint32_t kWindowBelow = 5;  // the window starts this many exponents below the last chunk's mode
-constexpr uint32_t kNoWindow = 0x100; // a window base that no exponent reaches (the first chunk)
+constexpr uint32_t kWindow = 8;        // exponents counted in lane-private counters
+constexpr uint32_t kWindowBelow = 5;   // the window starts this many exponents below the last chunk's mode
+constexpr uint32_t kNoWindow = 0x100;  // a window base that no exponent reaches (before the first mode)
+constexpr uint32_t kHistWaves = 4;                       // waves per workgroup
+constexpr uint32_t kHistThreads = 64 * kHistWaves;
+constexpr uint32_t kHistRound = 1024;                    // weights a wave counts per round (16 per lane)
+constexpr uint32_t kHistRounds = kChunk / kHistRound;    // rounds per chunk
+constexpr uint32_t kHistAhead = 2;                       // rounds requested ahead (register sets)
+constexpr uint32_t kHistGroupsPerCU = 3;                 // workgroups per CU at most
+static_assert(kHistRounds % kHistAhead == 0, "a register set must hold the same round of every chunk");
 
-// Thread t's 16 weights of chunk c as two 16-byte loads (zeros past the
-// block's end, through a buffer range that stops there).
-__device__ __forceinline__ void hist_load(const uint16_t *x, uint64_t n, uint64_t c, uint32_t t, df11w::v4u &a,
-                                          df11w::v4u &b) {
-    const uint64_t first = c * kChunk;
+// Lane's 16 weights of round r of chunk c as two 16-byte loads, each wave
+// load one contiguous 1 KB piece (zeros past the block's end, through a
+// buffer range that stops there; a chunk past the last reads as zeros).
+__device__ __forceinline__ void hist_load(const uint16_t *x, uint64_t n, uint64_t c, uint32_t r, uint32_t lane,
+                                          df11w::v4u &a, df11w::v4u &b) {
+    const uint64_t first = c * kChunk + uint64_t{r} * kHistRound;
     const uint64_t left = first < n ? n - first : 0;
-    const df11w::Rsrc r = df11w::rsrc(x + (first < n ? first : 0), static_cast<uint32_t>(2 * (left < kChunk ? left : kChunk)));
-    a = __builtin_amdgcn_raw_buffer_load_b128(r, 32 * t, 0, 0);
-    b = __builtin_amdgcn_raw_buffer_load_b128(r, 32 * t + 16, 0, 0);
+    const df11w::Rsrc rs =
+        df11w::rsrc(x + (left ? first : 0), static_cast<uint32_t>(2 * (left < kHistRound ? left : kHistRound)));
+    a = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, 0);
+    b = __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 + 16 * lane, 0, 0);
 }
 
 // Largest value over the 64 lanes, in every lane (DPP row shifts and row
@@ -110,93 +117,151 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
     return __builtin_amdgcn_readlane(m, 63);
 }
 
-__global__ void __launch_bounds__(kThreads) hist_kernel(const uint16_t *x, uint64_t n, uint64_t *hist,
-                                                        uint16_t *chunk_hist) {
-    // Weight exponents cluster on a few values, and same-address LDS atomics
-    // are serialised.  So each wave counts a window of 8 exponents, from 5
-    // below the previous chunk's most frequent exponent, in lane-private LDS
-    // counters (counter d of lane l at word 64d + l: no two lanes ever share a
-    // bank or an address), and only exponents outside the window go to
-    // sub-histograms shared by the lanes (8 copies, one per lane & 7).  After
-    // each chunk a wave adds its window counters over its lanes (DPP) into
-    // copy 0; thread t then owns exponent t: it adds up and clears the copies
-    // of its bin, records the chunk's count, keeps a running total and offers
-    // the bin to the choice of the next window.  The first chunk of a
-    // workgroup has no window.  Each chunk's weights are requested a chunk
-    // ahead; the barriers order LDS only, so the chunk's count store is not
-    // waited for.
-    __shared__ uint32_t h[kHistCopies * kHistStride];
-    __shared__ uint32_t win[kThreads / 64][kWindow * 64];
-    __shared__ uint32_t wmax[kThreads / 64];
-    const uint32_t t = threadIdx.x, lane = t & 63u, wave = t >> 6;
-    uint32_t *mine = h + (t & (kHistCopies - 1)) * kHistStride;
-    uint32_t *wc = &win[wave][lane];
-    for (uint32_t i = t; i < kHistCopies * kHistStride; i += blockDim.x) h[i] = 0;
-    for (uint32_t d = 0; d < kWindow; ++d) wc[64 * d] = 0;
-    __syncthreads();
-    const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
-    uint64_t total = 0;
-    uint32_t base = kNoWindow;  // uniform
-    uint64_t c = blockIdx.x;
-    df11w::v4u a, b;
-    hist_load(x, n, c, t, a, b);
-    for (; c < n_chunks; c += gridDim.x) {
-        df11w::v4u na, nb;
-        hist_load(x, n, c + gridDim.x, t, na, nb);
-        const uint64_t i0 = c * kChunk + uint64_t{t} * kPerThread;
-        if (i0 + kPerThread <= n) {
-            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+// Orders one wave's LDS accesses across its lanes (no other wave reads them).
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The window's first exponent for a mode (the most frequent exponent so far).
+__device__ __forceinline__ uint32_t window_base(uint32_t mode) {
+    return __builtin_amdgcn_readfirstlane(min(mode > kWindowBelow ? mode - kWindowBelow : 0u, 256u - kWindow));
+}
+
+// Most frequent of the lane's four bins 4 lane .. 4 lane + 3 over the wave
+// (ties: the larger exponent).
+__device__ __forceinline__ uint32_t wave_mode(const uint32_t cnt[4], uint32_t lane) {
+    uint32_t m = 0;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t e = exponent_of(w[k / 2] >> (16 * (k & 1)));
-                const uint32_t d = e - base;
-                if (d < kWindow)
-                    atomicAdd(wc + 64 * d, 1u);  // this lane's own counter
-                else
-                    atomicAdd(&mine[e], 1u);
-            }
-        } else {
-            for (uint64_t i = i0; i < n && i < i0 + kPerThread; ++i) atomicAdd(&mine[exponent_of(x[i])], 1u);
-        }
-        if (base != kNoWindow) {  // uniform: the wave's window counts, summed over its lanes, into copy 0
-            uint32_t pair[kWindow / 2];
+    for (uint32_t k = 0; k < 4; ++k) m = max(m, (cnt[k] << 8) | (4 * lane + k));
+    return wave_max(m) & 0xFFu;
+}
+
+// One round: each of the lane's 16 exponents goes to its own counter when it
+// falls in the window, else to the wave's bins.
+__device__ __forceinline__ void hist_count(const df11w::v4u &a, const df11w::v4u &b, uint32_t base, uint32_t *wc,
+                                           uint32_t *bins) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (uint32_t j = 0; j < kWindow / 2; ++j) {  // counts of at most 16 per lane: two per word
-                pair[j] = wc[64 * (2 * j)] | (wc[64 * (2 * j + 1)] << 16);
-                wc[64 * (2 * j)] = 0;
-                wc[64 * (2 * j + 1)] = 0;
-            }
-#pragma unroll
-            for (uint32_t j = 0; j < kWindow / 2; ++j) {
-                const uint32_t sum = __builtin_amdgcn_readlane(df11w::wave_inclusive_scan(pair[j]), 63);
-                if (lane == 0) {
-                    atomicAdd(&h[base + 2 * j], sum & 0xFFFFu);
-                    atomicAdd(&h[base + 2 * j + 1], sum >> 16);
-                }
-            }
-        }
-        lds_barrier();
-        uint32_t cnt = 0;
-#pragma unroll
-        for (uint32_t k = 0; k < kHistCopies; ++k) {
-            cnt += h[k * kHistStride + t];
-            h[k * kHistStride + t] = 0;
-        }
-        if (chunk_hist) chunk_hist[c * 256 + t] = static_cast<uint16_t>(cnt);  // at most 4,096
-        total += cnt;
-        // the chunk's most frequent exponent (ties: the larger exponent)
-        const uint32_t top = wave_max((cnt << 8) | t);
-        if (lane == 0) wmax[wave] = top;
-        lds_barrier();
-        uint32_t best = 0;
-#pragma unroll
-        for (uint32_t k = 0; k < kThreads / 64; ++k) best = max(best, wmax[k]);
-        const uint32_t mode = best & 0xFFu;
-        base = __builtin_amdgcn_readfirstlane(min(mode > kWindowBelow ? mode - kWindowBelow : 0u, 256u - kWindow));
-        a = na;
-        b = nb;
+    for (int k = 0; k < 16; ++k) {
+        const uint32_t e = exponent_of(w[k / 2] >> (16 * (k & 1)));
+        const uint32_t d = e - base;
+        if (d < kWindow)
+            atomicAdd(wc + 64 * d, 1u);  // this lane's own counter
+        else
+            atomicAdd(bins + e, 1u);
     }
-    if (total) atomicAdd(reinterpret_cast<unsigned long long *>(hist + t), static_cast<unsigned long long>(total));
+}
+
+// The end of a chunk's count: lane l takes bins 4l .. 4l + 3 of the wave
+// (clearing them), stores them as the chunk's counts (through a buffer range,
+// none without chunk_hist, so that the store is not behind a branch) and adds
+// them to its totals.
+__device__ __forceinline__ void hist_chunk_out(uint32_t *bins, uint16_t *chunk_hist, uint64_t c, uint32_t lane,
+                                               uint64_t total[4], uint32_t cnt[4]) {
+    wave_lds_fence();
+    const uint4 v = *reinterpret_cast<const uint4 *>(bins + 4 * lane);
+    *reinterpret_cast<uint4 *>(bins + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    cnt[0] = v.x, cnt[1] = v.y, cnt[2] = v.z, cnt[3] = v.w;
+    const df11w::Rsrc ch = df11w::rsrc(chunk_hist ? chunk_hist + c * 256 : nullptr, chunk_hist ? 512u : 0u);
+    __builtin_amdgcn_raw_buffer_store_b64(df11w::v2u{cnt[0] | (cnt[1] << 16), cnt[2] | (cnt[3] << 16)}, ch, 8 * lane,
+                                          0, 0);
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k) total[k] += cnt[k];
+}
+
+__global__ void __launch_bounds__(kHistThreads) hist_kernel(const uint16_t *x, uint64_t n, uint64_t *hist,
+                                                        uint16_t *chunk_hist) {
+    // Each wave counts whole chunks on its own, with no workgroup barrier
+    // until the end.  Weight exponents cluster on a few values, and
+    // same-address LDS atomics are serialised, so a window of 8 exponents,
+    // from 5 below the wave's last mode, is counted in lane-private LDS
+    // counters (counter d of lane l at word 64 d + l: no two lanes share a
+    // bank or an address) and only exponents outside it go to the wave's 256
+    // bins.  After a chunk the wave adds its window counters over its lanes
+    // (DPP) into the bins, and lane l reads, clears and stores bins
+    // 4l .. 4l + 3 as the chunk's counts, adds them to its running totals and
+    // offers them to the choice of the next window.  A wave's first window
+    // comes from the bins of its first round.  A chunk is counted in 4 rounds
+    // of 1,024 weights, each requested two rounds ahead.  The block's last
+    // chunk, when not whole, is counted weight by weight after the loop (a
+    // buffer load that ends past the range does not return its first part).
+    // At the end the workgroup adds its waves' totals in LDS and then into
+    // the block's histogram.
+    __shared__ __align__(16) uint32_t win[kHistWaves][kWindow * 64];
+    __shared__ __align__(16) uint32_t bins_all[kHistWaves][256];
+    __shared__ unsigned long long tot[256];
+    const uint32_t t = threadIdx.x, lane = t & 63u;
+    // uniform per wave, so that the buffer resources built from it stay in
+    // scalar registers
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    uint32_t *wc = &win[wave][lane];
+    uint32_t *bins = bins_all[wave];
+#pragma unroll
+    for (uint32_t d = 0; d < kWindow; ++d) wc[64 * d] = 0;
+    *reinterpret_cast<uint4 *>(bins + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    for (uint32_t i = t; i < 256; i += kHistThreads) tot[i] = 0;
+    __syncthreads();
+
+    const uint64_t n_full = n / kChunk;  // whole chunks
+    const uint64_t stride = uint64_t{gridDim.x} * kHistWaves;
+    uint64_t total[4] = {0, 0, 0, 0};
+    uint32_t cnt[4];
+    uint32_t base = kNoWindow;  // uniform
+    uint64_t c = uint64_t{blockIdx.x} * kHistWaves + wave;
+    // round r of a chunk is counted from register set r mod kHistAhead, which
+    // is then refilled with the round kHistAhead rounds later (of this chunk
+    // or the next one)
+    df11w::v4u a[kHistAhead], b[kHistAhead];
+#pragma unroll
+    for (uint32_t k = 0; k < kHistAhead; ++k) {
+        // in this order, as in the loop: a wait for one round then leaves the
+        // later ones in flight on both paths into the loop
+        hist_load(x, n, c, k, lane, a[k], b[k]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; c < n_full; c += stride) {
+#pragma unroll
+        for (uint32_t r = 0; r < kHistRounds; ++r) {
+            const uint32_t k = r % kHistAhead, rn = r + kHistAhead;
+            hist_count(a[k], b[k], base, wc, bins);
+            hist_load(x, n, rn < kHistRounds ? c : c + stride, rn % kHistRounds, lane, a[k], b[k]);
+            if (r == 0 && base == kNoWindow) {  // uniform: the wave's first window, from its first round
+                wave_lds_fence();
+                const uint4 v = *reinterpret_cast<const uint4 *>(bins + 4 * lane);
+                const uint32_t first[4] = {v.x, v.y, v.z, v.w};
+                base = window_base(wave_mode(first, lane));
+            }
+        }
+
+        // the window counters, summed over the lanes two at a time (at most
+        // 64 per lane and 4,096 per chunk: 16-bit halves), into the bins
+#pragma unroll
+        for (uint32_t j = 0; j < kWindow / 2; ++j) {
+            const uint32_t pair = wc[64 * (2 * j)] | (wc[64 * (2 * j + 1)] << 16);
+            wc[64 * (2 * j)] = 0;
+            wc[64 * (2 * j + 1)] = 0;
+            const uint32_t sum = __builtin_amdgcn_readlane(df11w::wave_inclusive_scan(pair), 63);
+            if (lane == 0) {
+                atomicAdd(bins + base + 2 * j, sum & 0xFFFFu);
+                atomicAdd(bins + base + 2 * j + 1, sum >> 16);
+            }
+        }
+        hist_chunk_out(bins, chunk_hist, c, lane, total, cnt);
+        base = window_base(wave_mode(cnt, lane));
+    }
+    if (c == n_full && n_full * kChunk < n) {  // uniform: this wave's sequence holds the last, partial chunk
+        for (uint64_t i = n_full * kChunk + lane; i < n; i += 64) atomicAdd(bins + exponent_of(x[i]), 1u);
+        hist_chunk_out(bins, chunk_hist, c, lane, total, cnt);
+    }
+    // the waves' totals, then one global atomic per nonzero bin
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k)
+        if (total[k]) atomicAdd(&tot[4 * lane + k], static_cast<unsigned long long>(total[k]));
+    __syncthreads();
+    for (uint32_t i = t; i < 256; i += kHistThreads)
+        if (tot[i]) atomicAdd(reinterpret_cast<unsigned long long *>(hist + i), tot[i]);
 }
 
 // ---------------------------------------------------------------- padding
@@ -685,10 +750,9 @@ hipError_t launch(void (*kernel)(A...), uint32_t grid, uint32_t block, hipStream
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3(grid), dim3(block), argv, 0, st);
 }
 
-// Workgroups for the persistent pack pass: as many as can be resident on
-// the device (taken once per device; a failed query falls back to a fixed
-// count and clears only its own error).
-uint32_t pack_groups() {
+// Compute units of the current device (taken once per device; a failed query
+// falls back to 256 and clears only its own error).
+uint32_t cu_count() {
     static std::mutex mu;
     static uint32_t cached[64] = {};
     int dev = 0;
@@ -698,18 +762,37 @@ uint32_t pack_groups() {
     }
     std::lock_guard<std::mutex> lk(mu);
     if (dev >= 0 && dev < 64 && cached[dev]) return cached[dev];
-    int cus = 0, per_cu = 0;
+    int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
         (void)hipGetLastError();
         cus = 256;
     }
+    if (dev >= 0 && dev < 64) cached[dev] = static_cast<uint32_t>(cus);
+    return static_cast<uint32_t>(cus);
+}
+
+// Workgroups for the persistent pack pass: as many as can be resident on
+// the device (taken once per device; a failed query falls back to a fixed
+// count and clears only its own error).
+uint32_t pack_groups() {
+    const uint32_t cus = cu_count();
+    static std::mutex mu;
+    static uint32_t cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        dev = 0;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    if (dev >= 0 && dev < 64 && cached[dev]) return cached[dev];
+    int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&pack_kernel),
                                                      static_cast<int>(kPackThreads), 0) != hipSuccess ||
         per_cu < 1) {
         (void)hipGetLastError();
         per_cu = 4;
     }
-    const uint32_t g = static_cast<uint32_t>(cus) * static_cast<uint32_t>(per_cu);
+    const uint32_t g = cus * static_cast<uint32_t>(per_cu);
     if (dev >= 0 && dev < 64) cached[dev] = g;
     return g;
 }
@@ -731,7 +814,10 @@ extern "C" df11_status df11_gpu_histogram(const uint16_t *x, uint64_t n, uint64_
     hipError_t err = launch(hist_zero, 1, 256, st, hist);
     const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
     if (err == hipSuccess && n)
-        err = launch(hist_kernel, static_cast<uint32_t>(std::min<uint64_t>(n_chunks, 2048)), kThreads, st, x, n,
+        err = launch(hist_kernel,
+                     static_cast<uint32_t>(std::min<uint64_t>((n_chunks + kHistWaves - 1) / kHistWaves,
+                                                              uint64_t{kHistGroupsPerCU} * cu_count())),
+                     kHistThreads, st, x, n,
                      hist, chunk_hist);
     if (err != hipSuccess) {
         df11i::last_hip_error = static_cast<int32_t>(err);

@@ -142,14 +142,15 @@ def test_histogram_when_the_exponent_mode_moves_between_chunks(torch):
     check(torch, x, "moving modes", counts=True)
 
 
-def test_histogram_window_follows_each_workgroups_chunks(torch):
-    """With more chunks than histogram workgroups (2,048), each workgroup
-    counts several chunks in turn and places each chunk's window from the
-    one before: here the scale changes every 2,048 chunks, so the chunks of
-    one workgroup jump between scales, one exponent (0, 127, 255), every
-    pattern and heavy tails, and the windows move up, down, to both ends and
-    miss most weights; counts per chunk and in total must still equal
-    numpy's."""
+def test_histogram_window_follows_each_waves_chunks(torch):
+    """With more chunks than histogram waves (3 workgroups of 4 waves per CU:
+    3,072 on 256 CUs), each wave counts several chunks in turn and places
+    each chunk's window from the one before: here the scale changes every
+    2,048 chunks, so the chunks of one wave jump between scales, one exponent
+    (0, 127, 255), every pattern and heavy tails, and the windows move up,
+    down, to both ends and miss most weights; the block's last chunk is
+    partial and is counted by the wave whose turn it is.  Counts per chunk
+    and in total must still equal numpy's."""
     rng = np.random.default_rng(33)
     groups, chunk = 2048, 4096
     kinds = ["n-2", "n-30", "single255", "all", "n-9", "single0", "t", "n-2", "single127", "n-5"]
@@ -173,7 +174,7 @@ def test_histogram_window_follows_each_workgroups_chunks(torch):
     xd = torch.from_numpy(x.view(np.int16)).to("cuda")
     h = torch.empty(256, dtype=torch.int64, device="cuda")
     ch = torch.full((hdb.df11_gpu_chunk_hist_bytes(x.size) // 2,), -1, dtype=torch.int16, device="cuda")
-    say(f"histogram, several chunks per workgroup: n={x.size}")
+    say(f"histogram, several chunks per wave: n={x.size}")
     hdb.df11_gpu_histogram(xd, h, ch)
     torch.cuda.synchronize()
     e = ((x >> 7) & 0xFF).astype(np.int64)
