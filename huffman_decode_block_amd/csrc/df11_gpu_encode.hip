@@ -47,6 +47,7 @@ constexpr uint32_t kSegChunks = kThreads;             // chunks per segment of t
 constexpr uint32_t kPackThreads = 512;                // pack: threads per workgroup
 constexpr uint32_t kPackPer = kChunk / kPackThreads;  // pack: weights per thread (8)
 constexpr uint32_t kScanThreads = 1024;
+constexpr uint32_t kBitsThreads = 1024;               // bits: threads per workgroup (one segment)
 
 struct EncParams {
     const uint16_t *x;
@@ -343,20 +344,23 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t *ws
 // ---------------------------------------------------------------- chunk bits
 // One thread per chunk: its bits are the sum over exponents of count x code
 // length; then the exclusive prefix within the segment (one workgroup).
-__global__ void __launch_bounds__(kThreads) bits_kernel(EncParams p) {
+__global__ void __launch_bounds__(kBitsThreads) bits_kernel(EncParams p) {
     // The bits of each chunk of this segment from its 256 counts: 8 lanes per
     // chunk, each reading 32 counts (64 contiguous bytes, so that a wave reads
     // 8 chunks' counts in one piece), summed over the 8 lanes with DPP; then
-    // the block scan of the segment's 256 chunk totals.
+    // the block scan of the segment's 256 chunk totals.  16 waves per
+    // segment, so that a chunk's counts are requested by two threads' loops at
+    // most and enough reads are in flight (a segment per 4 waves left most CUs
+    // with one or no workgroup).
     __shared__ uint32_t len[256];
     __shared__ uint32_t cbits[kSegChunks];
-    __shared__ uint32_t wsum[kThreads / 64];
+    __shared__ uint32_t wsum[kBitsThreads / 64];
     const uint32_t t = threadIdx.x;
-    len[t] = p.len[t];
+    if (t < 256) len[t] = p.len[t];
     __syncthreads();
     const uint32_t sub = t & 7u;  // this lane's eighth of a chunk's counts
     const uint64_t seg0 = uint64_t{blockIdx.x} * kSegChunks;
-    for (uint32_t k = t >> 3; k < kSegChunks; k += kThreads / 8) {
+    for (uint32_t k = t >> 3; k < kSegChunks; k += kBitsThreads / 8) {
         const uint64_t c = seg0 + k;
         uint32_t bits = 0;
         if (c < p.n_chunks) {
@@ -381,8 +385,8 @@ __global__ void __launch_bounds__(kThreads) bits_kernel(EncParams p) {
     __syncthreads();
     const uint64_t c = seg0 + t;
     uint32_t seg_bits;
-    const uint32_t pre = block_exclusive_sum<kThreads / 64>(cbits[t], wsum, seg_bits);
-    if (c < p.n_chunks) p.chunk_pre[c] = pre;
+    const uint32_t pre = block_exclusive_sum<kBitsThreads / 64>(t < kSegChunks ? cbits[t] : 0u, wsum, seg_bits);
+    if (t < kSegChunks && c < p.n_chunks) p.chunk_pre[c] = pre;
     if (t == 0) p.seg_sum[blockIdx.x] = seg_bits;
 }
 
@@ -911,7 +915,7 @@ df11_status gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint1
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     const uint32_t chunks = static_cast<uint32_t>(p.n_chunks);
     hipError_t err = hipSuccess;
-    if (chunks) err = launch(bits_kernel, static_cast<uint32_t>(p.n_segs), kThreads, st, p);
+    if (chunks) err = launch(bits_kernel, static_cast<uint32_t>(p.n_segs), kBitsThreads, st, p);
     if (err == hipSuccess && chunks) err = launch(top_kernel, 1, kScanThreads, st, p);
     if (err == hipSuccess) err = launch(bounds_kernel, grid_for(p.n_chunks, 1u << 20), kThreads, st, p);
     if (err == hipSuccess && chunks) {
