@@ -358,9 +358,21 @@ def overlap_bench(args, dev) -> None:
             for v in views:
                 F.linear(acts[v.shape[1]], v)
 
+        # the GEMMs alone read the weights from the two decode buffers in
+        # turn, as every schedule below does (the same weights for every block
+        # would stay partly in the Infinity Cache from one block to the next)
+        buf_views = []
+        for b in range(2):
+            hdb.df11_decode_block(blks[b], out=ahead.bufs[b][: blk.n_total], stream=stream)
+            buf_views.append(hdb.matrix_views(ahead.bufs[b][: blk.n_total], blk, shapes))
+        torch.cuda.synchronize()
+        for b in range(2):
+            for v, r in zip(buf_views[b], ref_views):
+                assert torch.equal(v.view(torch.int16), r.view(torch.int16))
+
         def gemms_only():
             for i in range(nb):
-                consume(i, ref_views)
+                consume(i, buf_views[i % 2])
 
         def decodes_only():
             for i in range(nb):
@@ -370,7 +382,6 @@ def overlap_bench(args, dev) -> None:
             for _ in range(3):
                 f()
         torch.cuda.synchronize()
-        t_g, t_d = timed(gemms_only) / nb, timed(decodes_only) / nb
         # The ahead-decode's footprint: the whole GPU, or a capped number of
         # workgroups (it then streams on fewer CUs and leaves the rest to the
         # GEMMs, which matters once they are compute-bound).
@@ -383,19 +394,35 @@ def overlap_bench(args, dev) -> None:
             per_launch[(wv, mg)] = timed(lambda: ahead.run(consume, stream=stream)) / nb
         best = min(per_launch, key=per_launch.get)
         t_p = per_launch[best]
-        # the same blocks decoded inline, on the consumer's stream right
-        # before each consumer (the serial order, default launch)
-        ahead.launch = None
-        ahead.mode = "inline"
-        for _ in range(2):
-            ahead.run(consume, stream=stream)
-        t_s = timed(lambda: ahead.run(consume, stream=stream)) / nb
         # auto: both schedules timed once for this batch (the ahead decode with
-        # the best launch found above), the faster kept, then timed like the others
+        # the best launch found above), the faster kept
         ahead.launch = None if best == (0, 0) else (best[0], best[1], 0, 0)
         ahead.mode = "auto"
         picked = ahead.calibrate(consume, stream=stream, key=bs)
-        t_a = timed(lambda: ahead.run(consume, stream=stream, key=bs)) / nb
+        auto_launch = ahead.launch
+
+        def serial():
+            # the same blocks decoded inline, on the consumer's stream right
+            # before each consumer (the serial order, default launch)
+            ahead.mode = "inline"
+            ahead.run(consume, stream=stream)
+
+        def auto():
+            ahead.launch, ahead.mode = auto_launch, "auto"
+            ahead.run(consume, stream=stream, key=bs)
+
+        for f in (serial, auto):
+            for _ in range(2):
+                f()
+        # the four compared schedules timed in turn, round after round, each
+        # keeping its best, so that a drift of the clocks or of the GEMMs'
+        # speed during the run does not favour whichever was timed last
+        t_g = t_d = t_s = t_a = float("inf")
+        for _ in range(5):
+            t_g = min(t_g, timed(gemms_only, reps=1) / nb)
+            t_d = min(t_d, timed(decodes_only, reps=1) / nb)
+            t_s = min(t_s, timed(serial, reps=1) / nb)
+            t_a = min(t_a, timed(auto, reps=1) / nb)
         ahead.launch = None
         name = lambda k: f"{k[0] or 'default'} waves/group, " + (f"{k[1]} groups" if k[1] else "default grid")  # noqa: E731
         res = {

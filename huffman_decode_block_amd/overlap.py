@@ -35,6 +35,10 @@ class DecodeAhead:
             Overlap pays when the consumer leaves memory bandwidth or compute
             units idle, and costs when it does not (a compute-bound consumer
             at large batch shares its units with the decode).
+    launch  launch geometry of the side-stream decodes (as for
+            ``df11_decode_block``), e.g. a capped grid that leaves compute
+            units to the consumer; None for the library's default.  Inline
+            decodes share the GPU with nothing and always use the default.
     """
 
     MODES = ("ahead", "inline", "auto")
@@ -126,7 +130,7 @@ class DecodeAhead:
             if released[b] is not None and on is not stream:  # the consumer of block k-2 is done with it
                 on.wait_event(released[b])
             buf = self.bufs[b][: int(self.blocks[i].raw.n_total)]
-            df11_decode_block(self.blocks[i], out=buf, stream=on, launch=self.launch)
+            df11_decode_block(self.blocks[i], out=buf, stream=on, launch=self.launch if on is not stream else None)
             if on is stream:
                 return buf, None
             ev = torch.cuda.Event()

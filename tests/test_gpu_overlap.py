@@ -113,3 +113,38 @@ def test_auto_mode_picks_a_schedule_per_key_and_mixed_runs_stay_exact(torch):
     for i, ws in seen:
         for w, ref in zip(ws, originals[i]):
             assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), f"block {i} weights differ"
+
+
+def test_launch_geometry_applies_to_side_stream_decodes_only(torch, monkeypatch):
+    """A capped launch is for decodes that share the GPU with the consumer:
+    the side-stream decodes take it, inline decodes use the library default;
+    the consumers still see exact weights in both schedules."""
+    import huffman_decode_block_amd.overlap as ov
+    print("[gpu-test] decode-ahead launch geometry per schedule", flush=True)
+    blocks, originals = _blocks(torch, 3)
+    stream = torch.cuda.current_stream()
+    calls = []
+    real = ov.df11_decode_block
+
+    def recording(blk, out=None, stream=None, launch=None):
+        calls.append((stream, launch))
+        return real(blk, out=out, stream=stream, launch=launch)
+
+    monkeypatch.setattr(ov, "df11_decode_block", recording)
+    capped = (8, 512, 0, 0)
+    ahead = DecodeAhead(blocks, [SHAPES] * 3, launch=capped)
+    for mode in ("ahead", "inline"):
+        ahead.mode = mode
+        calls.clear()
+        seen = []
+        ahead.run(lambda i, views: seen.append((i, [v.clone() for v in views])), stream=stream)
+        torch.cuda.synchronize()
+        assert len(calls) == 3
+        for on, launch in calls:
+            if mode == "ahead":
+                assert on is ahead.side and launch == capped
+            else:
+                assert on is stream and launch is None
+        for i, ws in seen:
+            for w, ref in zip(ws, originals[i]):
+                assert torch.equal(w.view(torch.int16), ref.view(torch.int16)), f"{mode}: block {i} weights differ"
