@@ -92,9 +92,10 @@ constexpr uint32_t kHistAhead = 2;                       // rounds requested ahe
 constexpr uint32_t kHistGroupsPerCU = 3;                 // workgroups per CU at most
 static_assert(kHistRounds % kHistAhead == 0, "a register set must hold the same round of every chunk");
 
-// Lane's 16 weights of round r of chunk c as two 16-byte loads, each wave
-// load one contiguous 1 KB piece (zeros past the block's end, through a
-// buffer range that stops there; a chunk past the last reads as zeros).
+// The lane's 16 weights of round r of chunk c as two 16-byte loads; each of
+// the wave's two loads reads one contiguous 1 KB piece (zeros past the
+// block's end, through a buffer range that stops there; a chunk past the last
+// reads as zeros).
 __device__ __forceinline__ void hist_load(const uint16_t *x, uint64_t n, uint64_t c, uint32_t r, uint32_t lane,
                                           df11w::v4u &a, df11w::v4u &b) {
     const uint64_t first = c * kChunk + uint64_t{r} * kHistRound;
