@@ -62,6 +62,7 @@ struct KParams {
     uint32_t n_tables;
     uint32_t stage_elems;  // 16-bit staging elements per wave, multiple of 8
     uint32_t out_phase;    // (address of out / 2) mod 32: where 64-byte sectors start
+    uint32_t unit_queue;   // 1: a workgroup's waves take its units in turn from an LDS counter
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -501,11 +502,19 @@ struct WavesPerEU {
     static constexpr int value = kDeepGlobal ? 4 : 8;
 };
 
-// The unit loop of one wave: decode unit u, then every stride-th unit after
-// it.  `cur` holds unit u's inputs, already requested.
+// The unit loop of one wave: decode unit u, then further units of its
+// workgroup.  A workgroup's units are group0 + r + j * stride for r below its
+// wave count and j = 0, 1, ...: position j * waves + r in the workgroup's
+// order.  Without the queue wave r takes positions r, r + waves, ...; with it
+// each wave takes its first position statically and then the workgroup's next
+// position from an LDS counter when it starts its next unit, so that the
+// workgroup's waves finish together: the workgroup holds its LDS and wave
+// slots until its last wave is done, and units take different times.
+// `cur` holds unit u's inputs, already requested.
 template <bool kDeepGlobal, bool kMulti, bool kCounts>
 __device__ __forceinline__ void unit_loop(const KParams &p, const uint32_t *lut, uint16_t *stage, uint32_t lane,
-                                          uint64_t u, uint64_t stride, UnitInputs cur) {
+                                          uint64_t u, uint64_t stride, UnitInputs cur, uint32_t *next_pos,
+                                          uint64_t group0, uint32_t wmask, uint32_t wshift) {
     const uint64_t last = p.n_units - 1;
     // Wait for the first unit's inputs here: the loop head then sees them
     // complete on both of its entries, and needs no wait that would also
@@ -520,7 +529,17 @@ __device__ __forceinline__ void unit_loop(const KParams &p, const uint32_t *lut,
         // unit rather than held in registers through it: that leaves phase 2
         // enough registers for eight waves per SIMD without spills.
         asm volatile("" : "+v"(lane));
-        uint64_t un = uniform_u64(u + stride);
+        uint64_t un;
+        if (p.unit_queue) {  // uniform
+            uint32_t k = 0;
+            if (lane == 0) k = atomicAdd(next_pos, 1u);
+            k = __builtin_amdgcn_readfirstlane(k);
+            // positions past the workgroup's last unit map past the block's
+            // last unit, and so do all later ones: every wave leaves the loop
+            un = uniform_u64(group0 + (k & wmask) + uint64_t{k >> wshift} * stride);
+        } else {
+            un = uniform_u64(u + stride);
+        }
         UnitInputs nxt;
         load_unit<kCounts>(p, un < last ? un : last, lane, nxt);
         decode_unit<kDeepGlobal, kMulti, kCounts>(p, lut, s_count_table, s_emit_table, stage, lane, u, cur, nxt);
@@ -560,6 +579,11 @@ df11_decode_kernel(KParams p) {
     // stream holds.  When any entry breaks this, the workgroup decodes with
     // the hierarchical tables alone (one code per lookup).  Each wave leaves
     // its verdict in its own LDS word, read by all after the one barrier.
+    // the workgroup's next unit position when its waves take units in turn
+    // (positions below `waves` are the waves' first units); published by the
+    // barrier of the table copy
+    __shared__ uint32_t s_next_pos;
+    if (threadIdx.x == 0) s_next_pos = waves;
     bool bad = false;
     {
         const uint32_t n_hier = lds_tables * 64u;  // 16-byte pieces
@@ -613,14 +637,18 @@ df11_decode_kernel(KParams p) {
 
     uint16_t *stage = reinterpret_cast<uint16_t *>(lds + lds_tables * 1024u) + wave * p.stage_elems;
     const uint64_t stride = uniform_u64(uint64_t{gridDim.x} * waves);
+    const uint64_t group0 = uniform_u64(uint64_t{blockIdx.x} * waves);
+    const uint32_t wshift = __builtin_amdgcn_readfirstlane(31u - __clz(waves));  // waves is a power of two
     if (u >= p.n_units) return;  // uniform across the wave
     if constexpr (kMulti) {
         if (__builtin_expect(bad, 0)) {  // uniform across the workgroup
-            unit_loop<kDeepGlobal, false, false>(p, lut, stage, lane, u, stride, cur);
+            unit_loop<kDeepGlobal, false, false>(p, lut, stage, lane, u, stride, cur, &s_next_pos, group0, waves - 1u,
+                                                 wshift);
             return;
         }
     }
-    unit_loop<kDeepGlobal, kMulti, kCounts>(p, lut, stage, lane, u, stride, cur);
+    unit_loop<kDeepGlobal, kMulti, kCounts>(p, lut, stage, lane, u, stride, cur, &s_next_pos, group0, waves - 1u,
+                                            wshift);
 }
 
 // ------------------------------------------------------------------ host side
@@ -737,7 +765,7 @@ df11_status decode_block(const df11_device_block *blk, uint16_t *out_bf16, uint6
     // LDS per workgroup: static (count and emit tables) + hierarchical tables
     // + one staging area per wave; it bounds how many waves are resident.
     const uint32_t lds_tables = deep_global ? 1u : blk->n_tables;
-    const uint32_t fixed_static = multi ? kMultiStaticBytes : 0u;
+    const uint32_t fixed_static = (multi ? kMultiStaticBytes : 0u) + 16u;  // + the unit position counter
     // staging: the unit's outputs after up to 7 slots of lead, rounded to
     // 8-output chunks
     const uint32_t stage_elems = static_cast<uint32_t>((blk->max_unit_count + 7 + 7) / 8 * 8);
@@ -791,6 +819,10 @@ df11_status decode_block(const df11_device_block *blk, uint16_t *out_bf16, uint6
         grid = std::min<uint64_t>(groups, std::max<uint64_t>(resident, (groups + kUnitsPerWave - 1) / kUnitsPerWave));
     if (launch && launch->max_groups) grid = std::min<uint64_t>(grid, launch->max_groups);
     grid = std::max<uint64_t>(grid, 1);
+    // Units taken in turn within a workgroup pay an LDS round trip before each
+    // next unit's loads: a gain of about 1 % when the waves have two units or
+    // more on average, a loss of about 1 % when most have one.
+    p.unit_queue = grid * waves * 2 <= blk->n_units ? 1u : 0u;
 
     // hipLaunchKernel reports the status of this launch only (hipGetLastError
     // would also return errors left behind by earlier runtime calls).

@@ -17,8 +17,9 @@
 //     unit's sign/mantissa bytes as 8-byte non-temporal loads; 16-byte
 //     non-temporal stores of the whole 64-byte sectors and 2-byte stores of
 //     the sectors the unit shares with its neighbours; the same workgroup
-//     size and grid rule.  What it lacks is the decoding itself (tables,
-//     counting, scan, staging).
+//     size, grid rule and unit order (a workgroup's units taken in turn from
+//     an LDS counter when its waves have two or more on average).  What it
+//     lacks is the decoding itself (tables, counting, scan, staging).
 //   stream: the same byte counts in whole tiles of 4,096 weights per wave:
 //     the tile's sign/mantissa bytes (8-byte non-temporal loads), its share of
 //     the stream and gap bytes (16-byte loads), its 8 KiB of output (16-byte
@@ -54,6 +55,7 @@ struct RefParams {
     uint64_t stream_used, gaps_used;  // section bytes a decode reads
     uint32_t stream_share, gaps_share;  // per tile, multiples of 16 (stream reference)
     uint32_t out_phase;                 // (address of out / 2) mod 32: 64-byte sector phase
+    uint32_t unit_queue;                // skeleton: the decode's unit order (units taken in turn)
 };
 
 // Two output values from four sign/mantissa bytes selected by `sel`: the
@@ -111,14 +113,29 @@ df11_skeleton_kernel(RefParams p) {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
     uint64_t u = uniform_u64(uint64_t{blockIdx.x} * waves + wave);
+    // as the decode: with the queue, each wave takes the workgroup's next unit
+    // position from an LDS counter (positions below `waves` are the first units)
+    __shared__ uint32_t s_next_pos;
+    if (threadIdx.x == 0) s_next_pos = waves;
+    __syncthreads();
     if (u >= p.n_units) return;  // uniform across the wave
     const uint64_t last = p.n_units - 1;
     const uint64_t stride = uniform_u64(uint64_t{gridDim.x} * waves);
+    const uint64_t group0 = uniform_u64(uint64_t{blockIdx.x} * waves);
+    const uint32_t wshift = __builtin_amdgcn_readfirstlane(31u - __clz(waves));  // waves is a power of two
     UnitLoads cur;
     load_unit(p, u, lane, cur);
     while (true) {
         asm volatile("" : "+v"(lane));
-        const uint64_t un = uniform_u64(u + stride);
+        uint64_t un;
+        if (p.unit_queue) {  // uniform
+            uint32_t k = 0;
+            if (lane == 0) k = atomicAdd(&s_next_pos, 1u);
+            k = __builtin_amdgcn_readfirstlane(k);
+            un = uniform_u64(group0 + (k & (waves - 1u)) + uint64_t{k >> wshift} * stride);
+        } else {
+            un = uniform_u64(u + stride);
+        }
         UnitLoads nxt;
         load_unit(p, un < last ? un : last, lane, nxt);  // one unit ahead, as the decode
         // the decode's first phase needs the window and gap: wait for them here
@@ -295,6 +312,7 @@ df11_status reference(const df11_device_block *blk, uint16_t *out, uint64_t cap,
         grid = std::min<uint64_t>(groups, std::max<uint64_t>(resident, (groups + per_wave - 1) / per_wave));
     if (launch && launch->max_groups) grid = std::min<uint64_t>(grid, launch->max_groups);
     grid = std::max<uint64_t>(grid, 1);
+    p.unit_queue = skeleton && grid * waves * 2 <= p.n_units ? 1u : 0u;  // the decode's rule
     void *args[] = {&p};
     const hipError_t err =
         hipLaunchKernel(fn, dim3(static_cast<uint32_t>(grid)), dim3(64 * waves), args, 0, static_cast<hipStream_t>(hip_stream));
