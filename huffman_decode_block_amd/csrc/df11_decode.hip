@@ -579,9 +579,10 @@ df11_decode_kernel(KParams p) {
     // stream holds.  When any entry breaks this, the workgroup decodes with
     // the hierarchical tables alone (one code per lookup).  Each wave leaves
     // its verdict in its own LDS word, read by all after the one barrier.
-    // the workgroup's next unit position when its waves take units in turn
-    // (positions below `waves` are the waves' first units); published by the
-    // barrier of the table copy
+    //
+    // The same barrier publishes the workgroup's next unit position, for
+    // waves that take its units in turn (positions below `waves` are the
+    // waves' first units).
     __shared__ uint32_t s_next_pos;
     if (threadIdx.x == 0) s_next_pos = waves;
     bool bad = false;
