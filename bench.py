@@ -83,11 +83,21 @@ def measured_traffic(workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
+# Sections read between two launches on the same copy, in Infinity Caches:
+# the cache keeps part of what a launch read for longer than one cache's worth
+# of later reads (C3 back to back over 2 copies, 600 MB of sections: the memory
+# skeleton took 124.6 us, over 4 copies 135.2, over 8 copies 136.2, after a
+# 1 GiB read 134.9), so the rotation covers several of them.
+ROTATION_CACHES = 6
+
+
 def rotation_copies(read_bytes: int, cap: int = 64) -> int:
     """Device copies of a block that the timed launches rotate over: enough
-    that their sections add up to twice the Infinity Cache, at least 2, at most
-    `cap` (blocks so small that the cap binds stay cached whatever the count)."""
-    return int(min(cap, max(2, -(-2 * INFINITY_CACHE_BYTES // max(int(read_bytes), 1)))))
+    that their sections add up to ROTATION_CACHES times the Infinity Cache, at
+    least 2, at most `cap` (blocks so small that the cap binds stay cached
+    whatever the count)."""
+    need = ROTATION_CACHES * INFINITY_CACHE_BYTES
+    return int(min(cap, max(2, -(-need // max(int(read_bytes), 1)))))
 
 
 def progress(msg: str) -> None:
@@ -121,12 +131,23 @@ class ColdSchedule:
     stay up; one synchronize at the end of each leg."""
 
     FLUSH_BYTES = 1 << 30
+    # What runs before each step ("read" is the schedule described above; the
+    # others attribute what a cold step pays): a read of 256 MiB (the Infinity
+    # Cache's size), or a sweep that reads one 8-byte element per 64 KiB over
+    # 4 GiB, which touches 65,536 pages but moves only ~4 MB, so that it evicts
+    # address translations and leaves the caches' contents as they were.
+    FLUSH_KINDS = ("read", "read-256mib", "touch-pages")
 
-    def __init__(self, dev, stream):
+    def __init__(self, dev, stream, kind: str = "read"):
         import torch
+        if kind not in self.FLUSH_KINDS:
+            raise ValueError(f"flush kind must be one of {self.FLUSH_KINDS}")
         self.torch = torch
         self.stream = stream
-        self.scratch = torch.ones(self.FLUSH_BYTES // 8, dtype=torch.int64, device=dev)
+        n = (4 << 30) if kind == "touch-pages" else (256 << 20) if kind == "read-256mib" else self.FLUSH_BYTES
+        self.scratch = torch.ones(n // 8, dtype=torch.int64, device=dev)
+        # one element per 64 KiB row for the sweep, the whole buffer otherwise
+        self.flush_view = self.scratch.view(-1, 8192)[:, 0] if kind == "touch-pages" else self.scratch
         self.flush_s = None  # leg B's mean of the last run (flush only), seconds
 
     def _leg(self, launch, k: int, start: int, inside: bool) -> list:
@@ -134,7 +155,7 @@ class ColdSchedule:
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
         for i in range(k):
             ev[i][0].record(self.stream)
-            self.scratch.sum()
+            self.flush_view.sum()
             if inside:
                 launch(start + i)
             ev[i][1].record(self.stream)
@@ -325,12 +346,14 @@ def overlap_bench(args, dev) -> None:
     x = di.generate(args.workload)
     enc = hdb.df11_encode_block(di.split(args.workload, x))
     blk = hdb.DeviceBlock.from_encoded(enc, device=dev)
-    # two device copies of the block in turn, so that no decode finds the
-    # previous one's sections in the Infinity Cache (as with different blocks)
-    blks = [blk, hdb.DeviceBlock.from_encoded(enc, device=dev)]
+    # device copies of the block in turn, so that no decode finds the
+    # sections of an earlier one in the Infinity Cache (as with different
+    # blocks)
+    n_copies = rotation_copies(algorithmic_bytes(enc.sections)["read"])
+    blks = [blk] + [hdb.DeviceBlock.from_encoded(enc, device=dev) for _ in range(n_copies - 1)]
     shapes = [(m.rows, m.cols) for m in wl.mats]
     nb = args.overlap_blocks
-    ahead = DecodeAhead([blks[i % 2] for i in range(nb)], [shapes] * nb, device=dev)
+    ahead = DecodeAhead([blks[i % n_copies] for i in range(nb)], [shapes] * nb, device=dev)
     ref = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
     ref_views = hdb.matrix_views(ref, blk, shapes)
     stream = torch.cuda.current_stream(dev)
@@ -376,7 +399,7 @@ def overlap_bench(args, dev) -> None:
 
         def decodes_only():
             for i in range(nb):
-                hdb.df11_decode_block(blks[i % 2], out=ahead.bufs[i % 2][: blk.n_total], stream=stream)
+                hdb.df11_decode_block(blks[i % n_copies], out=ahead.bufs[i % 2][: blk.n_total], stream=stream)
 
         for f in (gemms_only, decodes_only):  # warm up (clocks, GEMM algorithm choice)
             for _ in range(3):
@@ -429,6 +452,7 @@ def overlap_bench(args, dev) -> None:
             "metric": "exposed decode time per block, next block decoded on a side stream during this block's GEMMs",
             "value": round((t_p - t_g) * 1e6, 2), "unit": "us", "higher_is_better": False,
             "batch_tokens": bs, "blocks": nb, "workload": f"{args.workload}: {wl.description}",
+            "device_copies_rotated": n_copies,
             "gemms_only_us_per_block": round(t_g * 1e6, 2),
             "decode_only_us_per_block": round(t_d * 1e6, 2),
             "pipelined_us_per_block": round(t_p * 1e6, 2),
@@ -473,6 +497,13 @@ def main():
                     help="the headline leg: cold = caches flushed before every launch, each launch timed by its "
                          "own event pair; rotated = launches back to back over the device copies, one event pair "
                          "around all of them")
+    ap.add_argument("--flush", default="read", choices=list(ColdSchedule.FLUSH_KINDS),
+                    help="what runs before each cold launch: read = 1 GiB of unrelated data (the headline "
+                         "schedule); read-256mib = 256 MiB; touch-pages = one 8-byte element per 64 KiB over "
+                         "4 GiB (address translations evicted, cache contents kept)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="device copies of the block the launches rotate over (0 = enough that their sections "
+                         "cover several Infinity Caches)")
     ap.add_argument("--kernel", default="decode", choices=["decode", "skeleton", "stream"],
                     help="what the headline leg times: the decode, or one of the library's bandwidth references "
                          "(the line then reports that kernel, not the decode)")
@@ -488,6 +519,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
+    if args.copies < 0:
+        raise SystemExit("--copies must be 0 (automatic) or a positive count")
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode needs no cross-GPU exchange and "
@@ -543,8 +576,8 @@ def main():
 
     # A model decodes a different block each time.  The launches rotate over
     # device copies of the block (each with its own sections and output) whose
-    # sections together are at least twice the 256 MiB Infinity Cache.
-    n_copies = rotation_copies(ab["read"])
+    # sections together cover ROTATION_CACHES times the 256 MiB Infinity Cache.
+    n_copies = args.copies or rotation_copies(ab["read"])
     copies = [(hdb.DeviceBlock.from_encoded(enc, device=dev), new_output()) for _ in range(n_copies)]
 
     def decode(i):
@@ -578,7 +611,7 @@ def main():
         kernels["stream"] = reference(hdb.DF11_REFERENCE_STREAM)
     if args.kernel not in kernels:
         raise SystemExit("the bandwidth references cover the pages' format only")
-    cold = ColdSchedule(dev, stream)
+    cold = ColdSchedule(dev, stream, args.flush)
     pos = [0]
 
     def leg(name, schedule, k):
@@ -702,7 +735,7 @@ def main():
             "exp_entropy_bits": round(s.exp_entropy_bits, 4),
             "max_code_len": int(s.max_code_len),
             "decode_tables": int(s.n_tables),
-            "launch": {"kernel": args.kernel, "schedule": args.schedule,
+            "launch": {"kernel": args.kernel, "schedule": args.schedule, "flush": args.flush,
                        "waves_per_group": args.waves or "default", "max_groups": args.max_groups or "auto",
                        "oversubscribe": args.oversubscribe or "default",
                        "variant": {0: "default (multi-code)", 1: "one code per lookup",

@@ -99,13 +99,22 @@ def test_algorithmic_bytes_are_integers(bench):
     assert all(isinstance(v, int) for v in ab.values())
 
 
-def test_rotation_copies_exceed_twice_the_infinity_cache():
+def test_rotation_copies_cover_several_infinity_caches():
     import bench
-    cache = bench.INFINITY_CACHE_BYTES
-    assert bench.rotation_copies(299_316_096) == 2          # a Llama-3.1-8B-shaped block's sections
-    assert bench.rotation_copies(22_768_000) == 24          # one 4096 x 4096 matrix
-    for read in (1_000_000, 22_768_000, 100_000_000, 299_316_096, 4_000_000_000):
+    need = bench.ROTATION_CACHES * bench.INFINITY_CACHE_BYTES
+    assert bench.ROTATION_CACHES >= 4                        # two caches' worth still left hits
+    assert bench.rotation_copies(299_316_096) == 6          # a Llama-3.1-8B-shaped block's sections
+    assert bench.rotation_copies(1_200_000_000) == 2        # a Llama-3.1-70B-shaped block's
+    assert bench.rotation_copies(22_768_000) == 64          # one 4096 x 4096 matrix: the cap
+    for read in (1_000_000, 22_768_000, 100_000_000, 299_316_096, 720_000_000, 4_000_000_000):
         k = bench.rotation_copies(read)
-        assert k >= 2 and (k * read >= 2 * cache or k == 64)
-        assert k == 2 or (k - 1) * read < 2 * cache       # no more copies than needed
+        assert k >= 2 and (k * read >= need or k == 64)
+        assert k == 2 or (k - 1) * read < need              # no more copies than needed
     assert bench.rotation_copies(1) == 64 and bench.rotation_copies(0) == 64
+
+
+def test_cold_schedule_rejects_an_unknown_flush(bench):
+    # checked before anything is allocated
+    with pytest.raises(ValueError):
+        bench.ColdSchedule("cpu", None, "write-1gib")
+    assert bench.ColdSchedule.FLUSH_KINDS[0] == "read"  # the headline schedule is the default
