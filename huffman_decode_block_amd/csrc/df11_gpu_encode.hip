@@ -95,15 +95,16 @@ static_assert(kHistRounds % kHistAhead == 0, "a register set must hold the same 
 // The lane's 16 weights of round r of chunk c as two 16-byte loads; each of
 // the wave's two loads reads one contiguous 1 KB piece (zeros past the
 // block's end, through a buffer range that stops there; a chunk past the last
-// reads as zeros).
+// reads as zeros).  Non-temporal: the input is streamed once per pass and is
+// larger than the caches, so that it does not displace other lines.
 __device__ __forceinline__ void hist_load(const uint16_t *x, uint64_t n, uint64_t c, uint32_t r, uint32_t lane,
                                           df11w::v4u &a, df11w::v4u &b) {
     const uint64_t first = c * kChunk + uint64_t{r} * kHistRound;
     const uint64_t left = first < n ? n - first : 0;
     const df11w::Rsrc rs =
         df11w::rsrc(x + (left ? first : 0), static_cast<uint32_t>(2 * (left < kHistRound ? left : kHistRound)));
-    a = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, 0);
-    b = __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 + 16 * lane, 0, 0);
+    a = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, df11w::kNonTemporal);
+    b = __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 + 16 * lane, 0, df11w::kNonTemporal);
 }
 
 // Largest value over the 64 lanes, in every lane (DPP row shifts and row
@@ -301,7 +302,7 @@ __device__ __forceinline__ bool chunk_is_full(const EncParams &p, uint64_t c) { 
 __device__ __forceinline__ void load_full(const EncParams &p, uint64_t c, uint32_t t, uint32_t w[4]) {
     const bool full = chunk_is_full(p, c);
     const df11w::Rsrc r = df11w::rsrc(p.x + (full ? c * kChunk : 0), full ? 2 * kChunk : 0u);
-    const df11w::v4u a = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * t, 0, 0);
+    const df11w::v4u a = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * t, 0, df11w::kNonTemporal);
     w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w;
 }
 
