@@ -20,12 +20,14 @@
 //           the padding past what later passes write (stream, gaps, counts,
 //           sign/mantissa); presets unit_pos and the first-start records for
 //           the last unit and window, the only ones where no code may start
-//   pack    persistent, per chunk: each weight's bit offset (block scan),
-//           its sign/mantissa byte, its code and its start ORed into an LDS
-//           bit buffer and an LDS start bitmap; the buffer is written out
-//           (global atomic OR only on the two words shared with the
-//           neighbouring chunks) and the bitmap gives the first code start of
-//           every window (gap) and unit (position) in the chunk
+//   pack    persistent waves, one chunk per wave at a time: sign/mantissa
+//           bytes; each lane shifts the codes of its 64 consecutive weights
+//           into a register and writes the finished words into the wave's
+//           LDS frame (its start from a wave scan of the lanes' bits), which
+//           goes to HBM with global atomic OR only on the two words shared
+//           with the neighbouring chunks; the lane whose code is the first to
+//           start in a window writes that window's records (gap, unit
+//           position, first weight)
 //   finish  5-bit gap fields (8 windows per 5 bytes) and window counts
 // The aligned-units layout is produced by the host encoder only.
 #include <hip/hip_runtime.h>
@@ -44,8 +46,6 @@ constexpr uint64_t kMaxWeights = uint64_t{1} << 48;  // no block holds more (512
 constexpr uint32_t kPerThread = 16;                   // weights per thread in hist
 constexpr uint32_t kChunk = kThreads * kPerThread;    // 4,096 weights per chunk
 constexpr uint32_t kSegChunks = kThreads;             // chunks per segment of the two-level scan
-constexpr uint32_t kPackThreads = 512;                // pack: threads per workgroup
-constexpr uint32_t kPackPer = kChunk / kPackThreads;  // pack: weights per thread (8)
 constexpr uint32_t kScanThreads = 1024;
 constexpr uint32_t kBitsThreads = 1024;               // bits: threads per workgroup (one segment)
 
@@ -292,36 +292,8 @@ __device__ __forceinline__ void fill_padding(const EncParams &p, uint64_t tid, u
     }
 }
 
-// Weights of pack thread t of chunk c, eight as four packed words (two
-// weights each, the first in the low half).  load_full requests them for a
-// whole chunk (a chunk that is not whole reads as zeros, through a buffer
-// range of 0 bytes) and does not use them, so that the loads stay in flight;
-// load_partial reads the block's last, partial chunk element by element.
+// Whether chunk c holds kChunk weights (all but possibly the block's last).
 __device__ __forceinline__ bool chunk_is_full(const EncParams &p, uint64_t c) { return (c + 1) * kChunk <= p.n; }
-
-__device__ __forceinline__ void load_full(const EncParams &p, uint64_t c, uint32_t t, uint32_t w[4]) {
-    const bool full = chunk_is_full(p, c);
-    const df11w::Rsrc r = df11w::rsrc(p.x + (full ? c * kChunk : 0), full ? 2 * kChunk : 0u);
-    const df11w::v4u a = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * t, 0, df11w::kNonTemporal);
-    w[0] = a.x, w[1] = a.y, w[2] = a.z, w[3] = a.w;
-}
-
-__device__ __forceinline__ void load_partial(const EncParams &p, uint64_t c, uint32_t t, uint32_t m,
-                                             uint32_t w[4]) {
-    const uint64_t i0 = c * kChunk + uint64_t{t} * kPackPer;
-#pragma unroll
-    for (uint32_t k = 0; k < 4; ++k) {
-        const uint32_t lo = 2 * k < m ? p.x[i0 + 2 * k] : 0u;
-        const uint32_t hi = 2 * k + 1 < m ? p.x[i0 + 2 * k + 1] : 0u;
-        w[k] = lo | (hi << 16);
-    }
-}
-
-// Weights of chunk c that pack thread t takes (0..8).
-__device__ __forceinline__ uint32_t weights_of(const EncParams &p, uint64_t c, uint32_t t) {
-    const uint64_t i0 = c * kChunk + uint64_t{t} * kPackPer;
-    return i0 >= p.n ? 0u : static_cast<uint32_t>(p.n - i0 < kPackPer ? p.n - i0 : kPackPer);
-}
 
 // Block-wide exclusive sum of one value per thread (kWaves waves): a scan
 // inside each wave, then each wave adds the totals of the waves before it;
@@ -433,214 +405,309 @@ __global__ void __launch_bounds__(kThreads) bounds_kernel(EncParams p) {
 }
 
 // ---------------------------------------------------------------- pack
-// Persistent: each workgroup takes chunks c, c + grid, ... and requests the
-// next chunk's weights before packing the current one.  Per chunk, thread t
-// takes weights 8t .. 8t + 7: their codes form one run of bits that starts
-// at the chunk's offset plus the block prefix of the threads' run lengths.
-//
-// LDS frame: bit positions count from the start of the 64-bit window that
-// holds the chunk's first code, so a 32-bit word index serves the code
-// buffer and the code-start bitmap alike, and windows are word pairs.
-//
-// First-start records come from the bitmap: a window's gap is the position of
-// its first set bit, the first weight of the window is the chunk's first
-// weight plus the starts before it (prefix of popcounts), and a window that
-// opens a unit (64 windows) gives that unit's position.  A window belongs to
-// the chunk that holds its first start: the chunk's first window is left to
-// the previous chunk when that one's last code starts in it.
-// 32-bit words of a chunk's frame: at most 63 + 32 x 4,096 bits, the word after
-// the last one a code reaches, whole windows; a multiple of 4
-constexpr uint32_t kFrameWords = kChunk + 4;
-constexpr uint32_t kWinPerThread = (kFrameWords / 2 + kPackThreads - 1) / kPackThreads;
+// Persistent waves, each packing one 4,096-weight chunk at a time with no
+// workgroup barrier: lane l takes weights
+// 64 l .. 64 l + 63 of the chunk, whose codes form one run of at least 64
+// bits, so that a 32-bit word is shared by two neighbouring lanes at most.
+// The lane shifts its codes one after the other into a 64-bit register and
+// writes the last finished word into the wave's LDS frame after each code;
+// its first word, which the lane before also reaches into, is completed by
+// that lane's OR of its last partial word once the wave's runs are written.
+// Every weight's exponent is staged in LDS first (the chunk is read in
+// coalesced 16-byte pieces), so that each lane can take its 64 in order.
+// A window's record (gap, first weight, unit position) is written by the lane
+// whose code is the first to start in the window.  Chunks whose bits would
+// not fit the frame, and the block's last chunk when not whole, are packed
+// with global atomic ORs of each code instead.  A chunk's weights are
+// requested when the wave starts on it: holding the next chunk's 32 registers
+// through the packing loop would cost waves per SIMD (or spills).  Six waves
+// per SIMD (80 registers) leave room to request the table entries of the
+// next four weights before the current four are packed.
+constexpr uint32_t kRunWaves = 4;                                // waves per workgroup
+constexpr uint32_t kRunThreads = 64 * kRunWaves;
+constexpr uint32_t kRunPer = kChunk / 64;                        // weights per lane (64)
+constexpr uint32_t kRunStageWords = 64 * (kRunPer + 4) / 4;      // 1,088: 68 bytes of exponents per lane
+constexpr uint32_t kRunFrameWords = kRunStageWords - 64;         // then one spare word per lane
+constexpr uint32_t kRunFrameBits = 32 * (kRunFrameWords - 1);    // a chunk fits when its head and bits do
+constexpr uint32_t kRunGapSlots = (kRunFrameBits + 63) / 64 / 4 * 4 + 4;  // windows of a frame, bytes
+static_assert(kRunGapSlots * 64 >= kRunFrameBits + 63, "every window of a frame has a gap slot");
 
-__device__ __forceinline__ uint32_t clz64(uint64_t v) { return v ? static_cast<uint32_t>(__clzll(v)) : 64u; }
-
-// What the loop requests for the next chunk while packing the current one.
-// The loaded values are not combined here: any use makes the wave wait.
-// The per-chunk values are the same for every lane but go through vector
-// loads: a scalar load shares its wait counter with the LDS operations, so
-// the chunk's first LDS wait would also wait for the next chunk's values.
-struct ChunkInputs {
-    uint32_t w[4];            // the thread's eight weights, packed
-    uint32_t seg_lo, seg_hi;  // the chunk's first bit is seg_off + pre
-    uint32_t pre;
-    uint32_t xw;              // high half: the previous chunk's last weight (chunk 0: not used)
+// What a wave requests for a chunk: its 512 pieces of 8 weights (piece
+// lane + 64 k in w[k]; zeros for a chunk that is not whole), its first bit
+// (segment offset + prefix) and the 4-byte word whose high half is the
+// previous chunk's last weight.
+struct RunInputs {
+    df11w::v4u w[8];
+    uint32_t seg_lo, seg_hi, pre, xw;
 };
 
-__device__ __forceinline__ void load_inputs(const EncParams &p, uint64_t c, uint32_t t, ChunkInputs &in) {
-    const uint64_t cc = c < p.n_chunks ? c : 0;  // past the end: chunk 0 again, not used
-    const df11w::v2u so = __builtin_amdgcn_raw_buffer_load_b64(df11w::rsrc(p.seg_off + cc / kSegChunks, 8), 0, 0, 0);
+__device__ __forceinline__ void run_load(const EncParams &p, uint64_t c, uint32_t lane, RunInputs &in) {
+    const df11w::v2u so = __builtin_amdgcn_raw_buffer_load_b64(df11w::rsrc(p.seg_off + c / kSegChunks, 8), 0, 0, 0);
     in.seg_lo = so.x;
     in.seg_hi = so.y;
-    in.pre = __builtin_amdgcn_raw_buffer_load_b32(df11w::rsrc(p.chunk_pre + cc, 4), 0, 0, 0);
-    // the 4-byte word whose high half is the previous chunk's last weight
+    in.pre = __builtin_amdgcn_raw_buffer_load_b32(df11w::rsrc(p.chunk_pre + c, 4), 0, 0, 0);
     // (chunk 0: any readable word, not used)
-    const uint32_t *wl = cc ? reinterpret_cast<const uint32_t *>(p.x + cc * kChunk - 2) : p.chunk_pre;
+    const uint32_t *wl = c ? reinterpret_cast<const uint32_t *>(p.x + c * kChunk - 2) : p.chunk_pre;
     in.xw = __builtin_amdgcn_raw_buffer_load_b32(df11w::rsrc(wl, 4), 0, 0, 0);
-    load_full(p, c, t, in.w);
+    const bool full = chunk_is_full(p, c);
+    const df11w::Rsrc r = df11w::rsrc(p.x + (full ? c * kChunk : 0), full ? 2 * kChunk : 0u);
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k)
+        in.w[k] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (lane + 64 * k), 0, df11w::kNonTemporal);
 }
 
-// Packs chunk c.  Its stores of the code words and window records come after
-// `next` is taken (its loads were requested before this chunk's work, so
-// they have arrived): vmcnt counts loads and stores in issue order, and a wait
-// for the next chunk's loads after these stores would also wait for them.
-template <bool kWhole>
-__device__ __forceinline__ void pack_chunk(const EncParams &p, uint64_t c, const ChunkInputs &in,
-                                           const ChunkInputs &next, const uint2 *ent, uint32_t *bits,
-                                           uint32_t *starts, uint32_t *wsum, uint32_t *wsum2) {
-    const uint32_t t = threadIdx.x;
-    const uint64_t i0 = c * kChunk + uint64_t{t} * kPackPer;
-    const uint32_t m = kWhole ? kPackPer : weights_of(p, c, t);
-    const uint32_t *wc = in.w;
-    // readfirstlane returns a signed int: each half is taken as uint32_t before
-    // it is widened (a sign-extended low half would corrupt offsets past 2^31 bits)
-    const uint32_t seg_lo = __builtin_amdgcn_readfirstlane(in.seg_lo);
-    const uint32_t seg_hi = __builtin_amdgcn_readfirstlane(in.seg_hi);
-    const uint32_t chunk_pre = __builtin_amdgcn_readfirstlane(in.pre);
-    const uint64_t cb = ((static_cast<uint64_t>(seg_hi) << 32) | seg_lo) + chunk_pre;
-    const uint32_t len_last = ent[exponent_of(in.xw >> 16)].y;
-
-    // sign/mantissa bytes, (sign << 7) | mantissa, two weights per word
-    uint32_t smw[2];
+// The chunk's sign/mantissa bytes to HBM and its exponents into the staging:
+// exponent i of the chunk at byte i + 4 (i / 64), so that lane l reads its
+// 64 as 16 words at word 17 l + j (no two lanes in one bank).
+__device__ __forceinline__ void run_stage(const EncParams &p, uint64_t c, uint32_t lane, const RunInputs &in,
+                                          bool full, uint32_t *stage) {
+    // Addresses are a per-lane base plus a constant per piece, so that no
+    // per-piece address is kept in a register across chunks.  The block's
+    // last chunk, when not whole, is read and written element by element
+    // through buffer ranges that end at the block's end.
+    const uint32_t left = full ? kChunk : static_cast<uint32_t>(p.n - c * kChunk);
+    const df11w::Rsrc smr = df11w::rsrc(p.sm + c * kChunk, left);
+    const df11w::Rsrc xr = df11w::rsrc(p.x + c * kChunk, 2 * left);
+    uint32_t *st = stage + 2 * lane + (lane >> 3);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const uint32_t a = wc[2 * k], b = wc[2 * k + 1];
-        const uint32_t sa = ((a >> 8) & 0x00800080u) | (a & 0x007F007Fu);  // two sm bytes in 16-bit halves
-        const uint32_t sb = ((b >> 8) & 0x00800080u) | (b & 0x007F007Fu);
-        smw[k] = __builtin_amdgcn_perm(sb, sa, 0x06040200u);
-    }
-    if (kWhole || m == kPackPer) {
-        // written once and not read here: non-temporal (as whole lines per wave)
-        __builtin_nontemporal_store(df11w::v2u{smw[0], smw[1]}, reinterpret_cast<df11w::v2u *>(p.sm + i0));
-    } else {
-        for (uint32_t k = 0; k < m; ++k) p.sm[i0 + k] = static_cast<uint8_t>(smw[k / 4] >> (8 * (k & 3)));
-    }
-
-    // codes and lengths of the thread's weights (length 0 past the end)
-    uint32_t code[kPackPer], len[kPackPer];
-    uint32_t sum = 0;
+    for (uint32_t k = 0; k < 8; ++k) {
+        const uint32_t w0 = 8 * lane + 512 * k;  // weights w0 .. w0 + 7 of the chunk: piece lane + 64 k
+        uint32_t a[4] = {in.w[k].x, in.w[k].y, in.w[k].z, in.w[k].w};
+        if (!full) {
 #pragma unroll
-    for (uint32_t k = 0; k < kPackPer; ++k) {
-        const uint2 e = ent[exponent_of(wc[k / 2] >> (16 * (k & 1)))];
-        code[k] = (kWhole || k < m) ? e.x : 0u;
-        len[k] = (kWhole || k < m) ? e.y : 0u;
-        sum += len[k];
-    }
-
-    // this thread's first bit in the frame
-    uint32_t chunk_bits;
-    const uint32_t pre = block_exclusive_sum<kPackThreads / 64>(sum, wsum, chunk_bits);
-    const uint32_t head = static_cast<uint32_t>(cb & 63u);
-
-    // Each code is ORed into the code buffer at its own position (one 64-bit
-    // shift, two 32-bit ORs: the word it starts in and the next) and its
-    // start into the bitmap, so that no thread waits on another's words.
-    uint32_t pos = head + pre;
-#pragma unroll
-    for (uint32_t k = 0; k < kPackPer; ++k) {
-        const uint32_t l = len[k];
-        const uint32_t wi = pos >> 5, sh = pos & 31u;
-        const uint64_t v = static_cast<uint64_t>(code[k]) << ((64u - sh - l) & 63u);
-        atomicOr(&bits[wi], static_cast<uint32_t>(v >> 32));
-        atomicOr(&bits[wi + 1], static_cast<uint32_t>(v));
-        if (kWhole || k < m) atomicOr(&starts[wi], 0x80000000u >> sh);
-        pos += l;
-    }
-    lds_barrier();
-    asm volatile("" ::"v"(next.w[0]), "v"(next.w[1]), "v"(next.w[2]), "v"(next.w[3]), "v"(next.seg_lo),
-                 "v"(next.seg_hi), "v"(next.pre), "v"(next.xw));
-
-    // out to HBM as big-endian words, clearing the buffer for the next chunk;
-    // the first and last words are shared with the neighbouring chunks when
-    // the chunk does not start or end on a word boundary
-    const uint32_t k0 = head >> 5;
-    const uint32_t nwords = (head + chunk_bits + 31u) >> 5;
-    const bool head_shared = (cb & 31u) != 0;
-    const bool tail_shared = ((cb + chunk_bits) & 31u) != 0;
-    uint32_t *out = reinterpret_cast<uint32_t *>(p.stream) + 2 * (cb >> 6);
-    const uint64_t room = p.stream_bytes / 4 > 2 * (cb >> 6) ? p.stream_bytes / 4 - 2 * (cb >> 6) : 0;
-    for (uint32_t k = k0 + t; k < nwords; k += kPackThreads) {
-        const uint32_t v = __builtin_bswap32(bits[k]);
-        bits[k] = 0;
-        if (k >= room) continue;
-        if ((k == k0 && head_shared) || (k == nwords - 1 && tail_shared))
-            atomicOr(out + k, v);
-        else
-            out[k] = v;
-    }
-
-    // window records: thread t takes windows t*q .. t*q + q - 1 of the
-    // chunk's nwin, counts the starts in each, and the block scan of the
-    // counts gives every window the starts before it
-    const uint64_t wbase = cb >> 6;
-    const uint32_t nwin = (head + chunk_bits + 63u) >> 6;
-    const uint32_t q = (nwin + kPackThreads - 1) / kPackThreads;
-    const uint32_t jb = t * q;
-    uint64_t wv[kWinPerThread];
-    uint32_t cnt = 0;
-#pragma unroll
-    for (uint32_t i = 0; i < kWinPerThread; ++i) {
-        const uint32_t j = jb + i;
-        wv[i] = 0;
-        if (i < q && j < nwin) {
-            wv[i] = (static_cast<uint64_t>(starts[2 * j]) << 32) | starts[2 * j + 1];
-            starts[2 * j] = 0;
-            starts[2 * j + 1] = 0;
-            cnt += static_cast<uint32_t>(__popcll(wv[i]));
+            for (uint32_t h = 0; h < 4; ++h)
+                a[h] = __builtin_amdgcn_raw_buffer_load_b16(xr, 2 * (w0 + 2 * h), 0, 0) |
+                       (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(xr, 2 * (w0 + 2 * h + 1), 0, 0))
+                        << 16);
         }
-    }
-    uint32_t total;
-    uint32_t before = block_exclusive_sum<kPackThreads / 64>(cnt, wsum2, total);
-    const bool prev_has_start = c > 0 && head >= len_last;  // the previous chunk's last code starts in window 0
+        uint32_t smw[2];
 #pragma unroll
-    for (uint32_t i = 0; i < kWinPerThread; ++i) {
-        const uint32_t j = jb + i;
-        const uint64_t w = wbase + j;
-        if (wv[i] && (j > 0 || !prev_has_start) && w < p.n_windows) {
-            const uint64_t first = c * kChunk + before;  // the window's first weight
-            p.gap8[w] = static_cast<uint8_t>(clz64(wv[i]));
-            if (p.wfirst) p.wfirst[w] = first;
-            if ((w & 63u) == 0) p.unit_pos[w >> 6] = first;
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t x0 = a[2 * h], x1 = a[2 * h + 1];
+            const uint32_t s0 = ((x0 >> 8) & 0x00800080u) | (x0 & 0x007F007Fu);  // two sm bytes in 16-bit halves
+            const uint32_t s1 = ((x1 >> 8) & 0x00800080u) | (x1 & 0x007F007Fu);
+            smw[h] = __builtin_amdgcn_perm(s1, s0, 0x06040200u);
         }
-        before += static_cast<uint32_t>(__popcll(wv[i]));
+        if (full) {  // written once and not read here: non-temporal
+            __builtin_amdgcn_raw_buffer_store_b64(df11w::v2u{smw[0], smw[1]}, smr, w0, 0, df11w::kNonTemporal);
+        } else {
+#pragma unroll
+            for (uint32_t h = 0; h < 8; ++h)
+                __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(smw[h / 4] >> (8 * (h & 3))), smr, w0 + h, 0,
+                                                     0);
+        }
+        // piece lane + 64 k's exponents at word 2 pc + pc / 8 = (2 lane + lane / 8) + 136 k
+        st[136 * k] = __builtin_amdgcn_perm(a[1] >> 7, a[0] >> 7, 0x06040200u);      // weights 0..3
+        st[136 * k + 1] = __builtin_amdgcn_perm(a[3] >> 7, a[2] >> 7, 0x06040200u);  // and 4..7
     }
 }
 
-__global__ void __launch_bounds__(kPackThreads) pack_kernel(EncParams p) {
+// The packing loop of a chunk that fits the frame (see run_pack_kernel):
+// the lane's codes into the frame and its window records; returns the shift
+// register and the frame bit after the lane's last code.
+template <bool kCounts>
+__device__ __forceinline__ void run_lane_codes(const EncParams &p, const uint32_t ex[16], const uint2 *ent,
+                                               uint32_t *stage, uint8_t *gst, uint32_t lane, uint32_t pos0, int32_t nwb,
+                                               uint64_t wbase, uint64_t first0, uint64_t &acc_out, uint32_t &pos_out) {
+    uint64_t acc = 0;
+    uint32_t pos = pos0;
+    const uint32_t hw4 = 4 * (pos0 >> 5) + 4;
+    // Window records: nw is the frame window after the one where the code
+    // before started.  A code opens window pos / 64 when that is nw (it
+    // cannot start later: the code before is at most 32 bits), and its gap is
+    // then pos mod 64; codes that open none write their gap to the lane's
+    // spare word past the frame.  A lane's run spans fewer than 64 windows,
+    // so it opens at most one unit: uw, the first unit window from nw on,
+    // taken at weight uj.
+    uint32_t nw = static_cast<uint32_t>(nwb) >> 6;
+    const uint32_t uw = nw + ((64u - ((static_cast<uint32_t>(wbase) + nw) & 63u)) & 63u);
+    uint32_t uj = kRunPer;  // none
+    uint8_t *const spare = reinterpret_cast<uint8_t *>(stage + kRunFrameWords + lane);
+    const uint32_t first_lo = static_cast<uint32_t>(first0), first_hi = static_cast<uint32_t>(first0 >> 32);
+    // the frame's windows of wfirst, up to the last one of the block
+    const uint64_t wleft = kCounts && p.n_windows > wbase ? p.n_windows - wbase : 0;
+    const df11w::Rsrc wfr = df11w::rsrc(kCounts ? p.wfirst + wbase : nullptr,
+                                        static_cast<uint32_t>(8 * (wleft < kRunGapSlots ? wleft : kRunGapSlots)));
+    // table entries requested a group of four weights ahead (LDS latency)
+    uint2 ceq[2][4];
+#pragma unroll
+    for (uint32_t b = 0; b < 4; ++b) ceq[0][b] = ent[(ex[0] >> (8 * b)) & 0xFFu];
+#pragma unroll
+    for (uint32_t j = 0; j < kRunPer; ++j) {
+        if ((j & 3) == 0 && j + 4 < kRunPer) {
+#pragma unroll
+            for (uint32_t b = 0; b < 4; ++b) ceq[((j / 4) + 1) & 1][b] = ent[(ex[j / 4 + 1] >> (8 * b)) & 0xFFu];
+        }
+        const uint2 ce = ceq[(j / 4) & 1][j & 3];
+        const uint32_t pw = pos >> 6;
+        const bool opens = pw >= nw;
+        *(opens ? gst + pw : spare) = static_cast<uint8_t>(pos & 63u);
+        uj = opens && pw == uw ? j : uj;
+        if (kCounts)  // the window's first weight (first0 is a multiple of 64)
+            __builtin_amdgcn_raw_buffer_store_b64(df11w::v2u{first_lo | j, first_hi}, wfr, opens ? 8 * pw : df11w::kOff,
+                                                  0, 0);
+        nw += opens ? 1u : 0u;
+        acc = (acc << ce.y) | ce.x;
+        pos += ce.y;
+        // the last finished word (before the lane's first word is finished:
+        // that word, rewritten once it is)
+        const uint32_t a4 = max((pos >> 3) & ~3u, hw4) - 4;
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(stage) + a4) =
+            static_cast<uint32_t>(acc >> (pos & 31u));
+        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    if (uj < kRunPer) {
+        const uint64_t w = wbase + uw;
+        if (w < p.n_windows) p.unit_pos[w >> 6] = first0 + uj;
+    }
+    acc_out = acc;
+    pos_out = pos;
+}
+
+template <bool kCounts>  // with the window records of the stored window counts
+__global__ void __launch_bounds__(kRunThreads) __attribute__((amdgpu_waves_per_eu(6))) run_pack_kernel(EncParams p) {
     __shared__ uint2 ent[256];  // per exponent: code, length
-    __shared__ __align__(16) uint32_t bits[kFrameWords];
-    __shared__ __align__(16) uint32_t starts[kFrameWords];
-    __shared__ uint32_t wsum[kPackThreads / 64], wsum2[kPackThreads / 64];
-    const uint32_t t = threadIdx.x;
-    uint64_t c = blockIdx.x;
-    if (c >= p.n_chunks) return;  // uniform
-    if (t < 256) ent[t] = make_uint2(p.code[t], p.len[t]);
-    for (uint32_t k = t; k < kFrameWords / 4; k += blockDim.x) {
-        reinterpret_cast<uint4 *>(bits)[k] = make_uint4(0u, 0u, 0u, 0u);
-        reinterpret_cast<uint4 *>(starts)[k] = make_uint4(0u, 0u, 0u, 0u);
+    __shared__ uint8_t lentab[256];
+    __shared__ __align__(16) uint32_t stage_all[kRunWaves][kRunStageWords];
+    __shared__ __align__(16) uint32_t gap_all[kRunWaves][kRunGapSlots / 4];
+    const uint32_t t = threadIdx.x, lane = t & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    uint32_t *stage = stage_all[wave];
+    uint8_t *gst = reinterpret_cast<uint8_t *>(gap_all[wave]);  // per window of the frame: its gap, or 0xFF
+    if (t < 256) {
+        ent[t] = make_uint2(p.code[t], p.len[t]);
+        lentab[t] = p.len[t];
     }
-    ChunkInputs cur;
-    load_inputs(p, c, t, cur);
-    // the first chunk's inputs before the loop: its head then sees them
-    // complete, with no wait that would also drain the stores
-    asm volatile("" ::"v"(cur.w[0]), "v"(cur.w[1]), "v"(cur.w[2]), "v"(cur.w[3]), "v"(cur.seg_lo),
-                 "v"(cur.seg_hi), "v"(cur.pre), "v"(cur.xw));
-    lds_barrier();
-
+    for (uint32_t k = lane; k < kRunGapSlots / 4; k += 64) gap_all[wave][k] = 0xFFFFFFFFu;
+    __syncthreads();
+    const uint64_t stride = uint64_t{gridDim.x} * kRunWaves;
+    uint64_t c = uint64_t{blockIdx.x} * kRunWaves + wave;
+    if (c >= p.n_chunks) return;  // uniform per wave; no barrier follows
     while (true) {
-        // the next chunk's inputs, requested a whole chunk ahead
-        const uint64_t cn = c + gridDim.x;
-        ChunkInputs nxt;
-        load_inputs(p, cn, t, nxt);
-        if (chunk_is_full(p, c)) {  // uniform
-            pack_chunk<true>(p, c, cur, nxt, ent, bits, starts, wsum, wsum2);
-        } else {  // the block's last chunk
-            load_partial(p, c, t, weights_of(p, c, t), cur.w);
-            pack_chunk<false>(p, c, cur, nxt, ent, bits, starts, wsum, wsum2);
+        RunInputs cur;
+        run_load(p, c, lane, cur);
+        const bool full = chunk_is_full(p, c);  // uniform
+        wave_lds_fence();  // the previous chunk's frame has been read out
+        run_stage(p, c, lane, cur, full, stage);
+        // readfirstlane returns a signed int: each half is taken as uint32_t
+        // before it is widened
+        const uint32_t seg_lo = __builtin_amdgcn_readfirstlane(cur.seg_lo);
+        const uint32_t seg_hi = __builtin_amdgcn_readfirstlane(cur.seg_hi);
+        const uint32_t chunk_pre = __builtin_amdgcn_readfirstlane(cur.pre);
+        const uint32_t xw = __builtin_amdgcn_readfirstlane(cur.xw);
+        const uint64_t cb = ((static_cast<uint64_t>(seg_hi) << 32) | seg_lo) + chunk_pre;  // the chunk's first bit
+        const uint64_t cn = c + stride;
+        wave_lds_fence();
+
+        // the lane's 64 exponents (weight 64 lane + 4 j + b in byte b of ex[j])
+        uint32_t ex[16];
+#pragma unroll
+        for (uint32_t j = 0; j < 16; ++j) ex[j] = stage[17 * lane + j];
+        const uint64_t l0 = c * kChunk + uint64_t{kRunPer} * lane;  // the lane's first weight
+        const uint32_t m = full ? kRunPer : (l0 < p.n ? static_cast<uint32_t>(p.n - l0 < kRunPer ? p.n - l0 : kRunPer) : 0u);
+        uint32_t sum = 0, lastlen = 0;
+        if (full) {  // uniform
+#pragma unroll
+            for (uint32_t j = 0; j < kRunPer; ++j) {
+                const uint32_t l = lentab[(ex[j / 4] >> (8 * (j & 3))) & 0xFFu];
+                sum += l;
+                if (j == kRunPer - 1) lastlen = l;
+                if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // few lookups in flight: registers
+            }
+        } else {
+            for (uint32_t j = 0; j < m; ++j) sum += lentab[reinterpret_cast<const uint8_t *>(stage)[68 * lane + j]];
+            lastlen = lentab[reinterpret_cast<const uint8_t *>(stage)[68 * lane + kRunPer - 1]];
+        }
+        // the exponents are taken apart again in the packing loop rather
+        // than kept from here (64 more registers)
+#pragma unroll
+        for (uint32_t j = 0; j < 16; ++j) asm volatile("" : "+v"(ex[j]));
+        const uint32_t incl = df11w::wave_inclusive_scan(sum);
+        const uint32_t chunk_bits = __builtin_amdgcn_readlane(incl, 63);
+        const uint32_t head = static_cast<uint32_t>(cb & 63u);
+        const uint64_t wbase = cb >> 6;  // the frame's first window
+        // the code before the lane's first one: the previous lane's last, or
+        // the previous chunk's last weight (none before the block's first)
+        const uint32_t up = __shfl_up(lastlen, 1);
+        const uint32_t prevlen = lane ? up : (c ? static_cast<uint32_t>(lentab[exponent_of(xw >> 16)]) : 64u);
+        const uint32_t pos0 = head + incl - sum;  // frame bit of the lane's first code
+        // the first window boundary at or after the previous code's start: a
+        // code starting there or later opens a window
+        int32_t nwb = ((static_cast<int32_t>(pos0) - static_cast<int32_t>(prevlen)) >> 6) * 64 + 64;
+        const uint64_t first0 = c * kChunk + uint64_t{kRunPer} * lane;
+        const uint32_t k0 = head >> 5;
+        const uint32_t nwords = (head + chunk_bits + 31) >> 5;
+        const bool head_shared = (cb & 31u) != 0;
+        const bool tail_shared = ((cb + chunk_bits) & 31u) != 0;
+        uint32_t *out = reinterpret_cast<uint32_t *>(p.stream) + 2 * wbase;
+        const uint64_t room = p.stream_bytes / 4 > 2 * wbase ? p.stream_bytes / 4 - 2 * wbase : 0;
+
+        if (full && head + chunk_bits <= kRunFrameBits) {  // uniform
+            uint64_t acc;
+            uint32_t pos;
+            run_lane_codes<kCounts>(p, ex, ent, stage, gst, lane, pos0, nwb, wbase, first0, acc, pos);
+            // the lane's last partial word is the next lane's first word
+            // (ORed into it) or the chunk's last word (stored)
+            const uint32_t r = pos & 31u;
+            const uint32_t tailw = static_cast<uint32_t>(acc << (32u - r));
+            wave_lds_fence();
+            if (r) {
+                if (lane < 63)
+                    atomicOr(&stage[pos >> 5], tailw);
+                else
+                    stage[pos >> 5] = tailw;
+            }
+            wave_lds_fence();
+
+            // out to HBM as big-endian words; the first and last words are
+            // shared with the neighbouring chunks when the chunk does not
+            // start or end on a word boundary
+            for (uint32_t k = k0 + lane; k < nwords; k += 64) {
+                const uint32_t v = __builtin_bswap32(stage[k]);
+                if (k >= room) continue;
+                if ((k == k0 && head_shared) || (k == nwords - 1 && tail_shared))
+                    atomicOr(out + k, v);
+                else
+                    out[k] = v;
+            }
+            const uint32_t nwin = (head + chunk_bits + 63) >> 6;
+            for (uint32_t j = lane; j < nwin; j += 64) {
+                const uint8_t g = gst[j];
+                gst[j] = 0xFF;
+                if (g != 0xFF && wbase + j < p.n_windows) p.gap8[wbase + j] = g;
+            }
+        } else {
+            // Each code ORed into the stream in HBM.  The chunk's words that
+            // no neighbouring chunk shares are zeroed first (the shared ones
+            // were zeroed before this pass).
+            const uint32_t z0 = k0 + (head_shared ? 1u : 0u), z1 = nwords - (tail_shared ? 1u : 0u);
+            for (uint32_t k = z0 + lane; k < z1; k += 64)
+                if (k < room) out[k] = 0;
+            __threadfence();
+            uint32_t pos = pos0;
+            const uint8_t *lane_exp = reinterpret_cast<const uint8_t *>(stage) + 68 * lane;  // still staged
+            for (uint32_t j = 0; j < m; ++j) {
+                const uint2 ce = ent[lane_exp[j]];
+                if (static_cast<int32_t>(pos) >= nwb) {
+                    const uint32_t wr = static_cast<uint32_t>(nwb) >> 6;
+                    const uint64_t w = wbase + wr;
+                    if (w < p.n_windows) {
+                        p.gap8[w] = static_cast<uint8_t>(pos - static_cast<uint32_t>(nwb));
+                        if ((w & 63u) == 0) p.unit_pos[w >> 6] = first0 + j;
+                        if (p.wfirst) p.wfirst[w] = first0 + j;
+                    }
+                    nwb += 64;
+                }
+                const uint32_t wi = pos >> 5, sh = pos & 31u;
+                const uint64_t v = static_cast<uint64_t>(ce.x) << (64u - sh - ce.y);
+                if (wi < room) atomicOr(out + wi, __builtin_bswap32(static_cast<uint32_t>(v >> 32)));
+                if (static_cast<uint32_t>(v) && wi + 1 < room)
+                    atomicOr(out + wi + 1, __builtin_bswap32(static_cast<uint32_t>(v)));
+                pos += ce.y;
+            }
         }
         if (cn >= p.n_chunks) break;  // uniform
         c = cn;
-        cur = nxt;  // arrived: taken before this chunk's stores
     }
 }
 
@@ -780,7 +847,7 @@ uint32_t cu_count() {
 // Workgroups for the persistent pack pass: as many as can be resident on
 // the device (taken once per device; a failed query falls back to a fixed
 // count and clears only its own error).
-uint32_t pack_groups() {
+uint32_t run_groups() {
     const uint32_t cus = cu_count();
     static std::mutex mu;
     static uint32_t cached[64] = {};
@@ -792,11 +859,11 @@ uint32_t pack_groups() {
     std::lock_guard<std::mutex> lk(mu);
     if (dev >= 0 && dev < 64 && cached[dev]) return cached[dev];
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&pack_kernel),
-                                                     static_cast<int>(kPackThreads), 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&run_pack_kernel<false>),
+                                                     static_cast<int>(kRunThreads), 0) != hipSuccess ||
         per_cu < 1) {
         (void)hipGetLastError();
-        per_cu = 4;
+        per_cu = 6;
     }
     const uint32_t g = cus * static_cast<uint32_t>(per_cu);
     if (dev >= 0 && dev < 64) cached[dev] = g;
@@ -923,7 +990,10 @@ df11_status gpu_encode(const df11_gpu_plan *plan, const uint16_t *x, const uint1
     if (err == hipSuccess && chunks) {
         // a few workgroups per resident slot: enough to fill the GPU, each
         // taking many chunks so that the next chunk's loads overlap the current
-        err = launch(pack_kernel, std::min<uint32_t>(chunks, pack_groups()), kPackThreads, st, p);
+        const uint32_t groups =
+            static_cast<uint32_t>(std::min<uint64_t>((chunks + kRunWaves - 1) / kRunWaves, run_groups()));
+        err = with_counts ? launch(run_pack_kernel<true>, groups, kRunThreads, st, p)
+                          : launch(run_pack_kernel<false>, groups, kRunThreads, st, p);
     }
     if (err == hipSuccess && nw)
         err = launch(finish_kernel, grid_for(with_counts ? nw : nw / 32 + 1, 4096), kThreads, st, p);
