@@ -16,9 +16,10 @@ The launches rotate over device copies of the block.  Prints one JSON line.
   roofline   algorithmic HBM bytes per launch (compressed sections read +
              BF16 written) / mean decode time, vs 8 TB/s; frac_rotated is the
              same for launches back to back over the copies without flushes
-  bandwidth_reference  two streaming kernels of the library that move the
+  bandwidth_reference  streaming kernels of the library that move the
              decode's bytes without decoding (its memory skeleton, and a plain
-             stream of the same bytes), timed in both schedules
+             stream of the same bytes), and the stream's writes alone and
+             reads alone, timed in both schedules
   cpu_baseline  the oracle's unit-parallel bit-serial decode of the same block
              on this host's cores (rank 0, N=1 only)
 """
@@ -609,6 +610,8 @@ def main():
     if not args.aligned_units and not with_counts:
         kernels["skeleton"] = reference(hdb.DF11_REFERENCE_SKELETON)
         kernels["stream"] = reference(hdb.DF11_REFERENCE_STREAM)
+        kernels["writes"] = reference(hdb.DF11_REFERENCE_WRITES)
+        kernels["reads"] = reference(hdb.DF11_REFERENCE_READS)
     if args.kernel not in kernels:
         raise SystemExit("the bandwidth references cover the pages' format only")
     cold = ColdSchedule(dev, stream, args.flush)
@@ -658,7 +661,7 @@ def main():
                 raise SystemExit("decode is not bit-exact after timing; refusing to report a number")
     refs = {}
     if len(kernels) > 1:
-        for name in ("skeleton", "stream"):
+        for name in ("skeleton", "stream", "writes", "reads"):
             if not args.headline_only:
                 for sched in ("cold", "rotated"):
                     if (name, sched) in times:
@@ -668,7 +671,14 @@ def main():
                     times[(name, sched)] = sum(t) / len(t)
             if args.headline_only and name != args.kernel:
                 continue
-            expect = torch.bitwise_and(xd, torch.tensor(-32641, dtype=torch.int16, device=dev))  # 0x807F
+            # skeleton and stream write each weight with its exponent field
+            # zero, writes zeros, reads nothing (the outputs keep the values
+            # the references before it wrote)
+            expect = (torch.zeros_like(xd) if name == "writes"
+                      else torch.bitwise_and(xd, torch.tensor(-32641, dtype=torch.int16, device=dev)))  # 0x807F
+            if name == "reads":
+                for j in range(n_copies):
+                    kernels["stream"](j)
             for j in range(n_copies):
                 kernels[name](j)
             for b, o in copies:
@@ -691,13 +701,15 @@ def main():
     head_bytes = ab["total"] if args.kernel == "decode" else ref_bytes
     achieved = head_bytes / k_head / 1e9
     frac = lambda t, nb=ab["total"]: round(nb / t / 1e9 / PEAK_HBM_GBS, 4) if t else None  # noqa: E731
+    out_bytes = 2 * n
     for name, r in refs.items():
-        r["bytes"] = ref_bytes
+        nb = {"writes": out_bytes, "reads": ref_bytes - out_bytes}.get(name, ref_bytes)
+        r["bytes"] = nb
         for sched in ("cold", "rotated"):
             if f"{sched}_us" in r:
-                r[f"GBps_{sched}"] = round(ref_bytes / r[f"{sched}_us"] / 1e3, 1)
+                r[f"GBps_{sched}"] = round(nb / r[f"{sched}_us"] / 1e3, 1)
                 kd = times.get(("decode", sched))
-                if kd:
+                if kd and name in ("skeleton", "stream"):
                     r[f"decode_over_reference_{sched}"] = round(ab["total"] / kd / 1e9 / r[f"GBps_{sched}"], 3)
     us = lambda v: round(v * 1e6, 2) if v else None  # noqa: E731
     kernel_name = {"decode": "df11_decode_kernel", "skeleton": "df11_skeleton_kernel",

@@ -113,6 +113,8 @@ EXPORTS = [
 
 DF11_REFERENCE_SKELETON = 1
 DF11_REFERENCE_STREAM = 2
+DF11_REFERENCE_WRITES = 3
+DF11_REFERENCE_READS = 4
 
 
 def lib():
@@ -479,10 +481,11 @@ def df11_decode_block_ex(block: DeviceBlock, out=None, stream=None, waves_per_gr
 
 
 def df11_bandwidth_reference(block: DeviceBlock, out, kind: int, stream=None, launch=None):
-    """A bandwidth reference for the decode of `block` (DF11_REFERENCE_SKELETON
-    or DF11_REFERENCE_STREAM): moves the decode's HBM bytes and writes into
-    `out` (a 16-bit device tensor) each weight with its exponent field zero.
-    Returns out."""
+    """A bandwidth reference for the decode of `block`: DF11_REFERENCE_SKELETON
+    or DF11_REFERENCE_STREAM move the decode's HBM bytes and write into `out`
+    (a 16-bit device tensor) each weight with its exponent field zero;
+    DF11_REFERENCE_WRITES writes zeros only, DF11_REFERENCE_READS reads the
+    sections only.  Returns out."""
     import torch
     if out.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not out.is_cuda:
         raise TypeError("out must be a 16-bit device tensor")
@@ -656,7 +659,7 @@ __all__ = [
     "df11_tables_size", "df11_build_tables", "df11_device_block_from_blob", "df11_decode_block",
     "df11_decode_block_ex", "df11_status_str", "df11_last_hip_error", "df11_hip_error_name",
     "df11_gpu_chunk_hist_bytes", "df11_gpu_histogram", "df11_gpu_plan_build", "df11_gpu_encode", "gpu_encode",
-    "GpuEncoded", "df11_bandwidth_reference", "df11_gpu_encode_noalloc", "DF11_NOALLOC_WORKSPACE_BYTES", "DF11_REFERENCE_SKELETON", "DF11_REFERENCE_STREAM",
+    "GpuEncoded", "df11_bandwidth_reference", "df11_gpu_encode_noalloc", "DF11_NOALLOC_WORKSPACE_BYTES", "DF11_REFERENCE_SKELETON", "DF11_REFERENCE_STREAM", "DF11_REFERENCE_WRITES", "DF11_REFERENCE_READS",
     "Encoded", "Sections",
     "DeviceBlock", "DF11Error", "matrix_views", "lib", "library_stamp",
 ]

@@ -25,6 +25,9 @@
 //     the stream and gap bytes (16-byte loads), its 8 KiB of output (16-byte
 //     non-temporal stores).  No unit boundaries, no shared sectors: the
 //     ceiling of this read/write mix on the GPU.
+//   writes, reads: the stream reference's stores alone (zeros) and its loads
+//     alone (nothing stored), so that the mix can be set against what each
+//     direction reaches by itself.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -56,6 +59,7 @@ struct RefParams {
     uint32_t stream_share, gaps_share;  // per tile, multiples of 16 (stream reference)
     uint32_t out_phase;                 // (address of out / 2) mod 32: 64-byte sector phase
     uint32_t unit_queue;                // skeleton: the decode's unit order (units taken in turn)
+    uint32_t reads_store_flag;          // stream, reads only: 0 (no store)
 };
 
 // Two output values from four sign/mantissa bytes selected by `sel`: the
@@ -202,6 +206,11 @@ df11_skeleton_kernel(RefParams p) {
 
 constexpr uint32_t kTileChunks = kTileWeights / 8;  // 512: 8 per lane
 
+// kMode: kMix moves both the section reads and the output writes; kWrites
+// only the output writes (zeros); kReads only the section reads.
+enum StreamMode : int { kMix = 0, kWrites = 1, kReads = 2 };
+
+template <int kMode>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8)))
 df11_stream_kernel(RefParams p) {
     const uint32_t lane = threadIdx.x & 63u;
@@ -217,13 +226,15 @@ df11_stream_kernel(RefParams p) {
         const Rsrc sr = rsrc(p.stream + s0, static_cast<uint32_t>(s_left < p.stream_share ? s_left : p.stream_share));
         const Rsrc gr = rsrc(p.gaps + g0, static_cast<uint32_t>(g_left < p.gaps_share ? g_left : p.gaps_share));
         uint32_t fold = 0;
-        for (uint32_t off = 16 * lane; off < p.stream_share; off += 1024) {
-            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
-            fold ^= v.x ^ v.y ^ v.z ^ v.w;
-        }
-        for (uint32_t off = 16 * lane; off < p.gaps_share; off += 1024) {
-            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(gr, off, 0, 0);
-            fold ^= v.x ^ v.y ^ v.z ^ v.w;
+        if (kMode != kWrites) {
+            for (uint32_t off = 16 * lane; off < p.stream_share; off += 1024) {
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, 0);
+                fold ^= v.x ^ v.y ^ v.z ^ v.w;
+            }
+            for (uint32_t off = 16 * lane; off < p.gaps_share; off += 1024) {
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(gr, off, 0, 0);
+                fold ^= v.x ^ v.y ^ v.z ^ v.w;
+            }
         }
         const uint64_t w0 = t * kTileWeights;
         const uint64_t left = p.n_total - w0;
@@ -232,7 +243,16 @@ df11_stream_kernel(RefParams p) {
         v2u smv[kTileChunks / 64];
 #pragma unroll
         for (uint32_t k = 0; k < kTileChunks / 64; ++k)
-            smv[k] = __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * (lane + 64 * k), 0, kNonTemporal);
+            smv[k] = kMode == kWrites ? v2u{0u, 0u}
+                                      : __builtin_amdgcn_raw_buffer_load_b64(smr, 8 * (lane + 64 * k), 0, kNonTemporal);
+        if (kMode == kReads) {
+            // the loaded values only decide a store that the host's flag
+            // (never set) enables, so that the loads are not dropped
+#pragma unroll
+            for (uint32_t k = 0; k < kTileChunks / 64; ++k) fold ^= smv[k].x ^ smv[k].y;
+            if (p.reads_store_flag && fold == 0) p.out[0] = 0;
+            continue;
+        }
         asm volatile("" ::"v"(fold));
         const Rsrc full = rsrc(p.out + w0, 16 * (n / 8));
 #pragma unroll
@@ -271,7 +291,9 @@ int cu_count() {
 
 df11_status reference(const df11_device_block *blk, uint16_t *out, uint64_t cap, uint32_t kind, void *hip_stream,
                       const df11_launch *launch) {
-    if (kind != DF11_REFERENCE_SKELETON && kind != DF11_REFERENCE_STREAM) return DF11_E_INVALID_ARG;
+    if (kind != DF11_REFERENCE_SKELETON && kind != DF11_REFERENCE_STREAM && kind != DF11_REFERENCE_WRITES &&
+        kind != DF11_REFERENCE_READS)
+        return DF11_E_INVALID_ARG;
     df11_status rc = df11i::check_device_block(blk, out, cap);
     if (rc != DF11_OK || blk->n_total == 0) return rc;
     if (blk->unit_end || blk->counts) return DF11_E_UNSUPPORTED;  // the pages' format only
@@ -298,9 +320,12 @@ df11_status reference(const df11_device_block *blk, uint16_t *out, uint64_t cap,
     p.gaps_share = share(p.gaps_used);
     p.out_phase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(out) >> 1) & 31u;
 
+    p.reads_store_flag = 0;
     const bool skeleton = kind == DF11_REFERENCE_SKELETON;
-    const void *fn = skeleton ? reinterpret_cast<const void *>(&df11_skeleton_kernel)
-                              : reinterpret_cast<const void *>(&df11_stream_kernel);
+    const void *fn = skeleton                          ? reinterpret_cast<const void *>(&df11_skeleton_kernel)
+                     : kind == DF11_REFERENCE_STREAM ? reinterpret_cast<const void *>(&df11_stream_kernel<kMix>)
+                     : kind == DF11_REFERENCE_WRITES ? reinterpret_cast<const void *>(&df11_stream_kernel<kWrites>)
+                                                     : reinterpret_cast<const void *>(&df11_stream_kernel<kReads>);
     const uint64_t items = skeleton ? p.n_units : p.n_tiles;
     const uint64_t per_wave = skeleton ? kUnitsPerWave : kTilesPerWave;
     const uint64_t groups = (items + waves - 1) / waves;

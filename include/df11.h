@@ -281,14 +281,15 @@ df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf1
                                  const df11_launch *launch);
 
 /* ---- Bandwidth references (measurement aids) -----------------------------
- * Two streaming kernels that move the HBM bytes of one df11_decode_block
- * launch of blk, without decoding, so that the decode's rate can be set
- * against what the same traffic reaches on the same GPU.  The decode reads
+ * Streaming kernels that move the HBM bytes of one df11_decode_block launch
+ * of blk (or one direction of them), without decoding, so that the decode's
+ * rate can be set against what the same traffic reaches on the same GPU.
+ * The decode reads
  * the compressed sections once and writes the block once, coalesced (hada.io
  * summary of the DFloat11 paper, section "Noyau GPU en deux etapes et
- * metadonnees auxiliaires").  Both write out_bf16[i] = the block's weight i
- * with its exponent field zero (sign and mantissa from sign_mant), for i in
- * [0, n_total), and nothing else.
+ * metadonnees auxiliaires").  The first two write out_bf16[i] = the block's
+ * weight i with its exponent field zero (sign and mantissa from sign_mant),
+ * for i in [0, n_total), and nothing else.
  *  DF11_REFERENCE_SKELETON: the decode's own HBM accesses unit by unit (one
  *    64-lane wave per unit of 64 windows: window words with their halo, gap
  *    bytes and the unit's positions one unit ahead, 8-byte sign/mantissa
@@ -297,6 +298,10 @@ df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf1
  *    decode's workgroup size and grid rule.
  *  DF11_REFERENCE_STREAM: the same byte counts moved in whole tiles of 4,096
  *    weights per wave (no unit boundaries, no shared sectors).
+ *  DF11_REFERENCE_WRITES: the stream reference's stores alone: out_bf16[i] =
+ *    0 for i in [0, n_total), no section read.
+ *  DF11_REFERENCE_READS: the stream reference's loads alone: the sections
+ *    read, out_bf16 left as it was.
  * Same arguments, checks, errors and stream semantics as df11_decode_block_ex
  * (launch: waves_per_group, max_groups and oversubscribe are used; variant is
  * ignored; NULL = automatic).  Blocks with stored window counts or the
@@ -304,6 +309,8 @@ df11_status df11_decode_block_ex(const df11_device_block *blk, uint16_t *out_bf1
  * DF11_E_INVALID_ARG. */
 #define DF11_REFERENCE_SKELETON 1u
 #define DF11_REFERENCE_STREAM 2u
+#define DF11_REFERENCE_WRITES 3u
+#define DF11_REFERENCE_READS 4u
 
 df11_status df11_bandwidth_reference(const df11_device_block *blk, uint16_t *out_bf16, uint64_t out_capacity,
                                      uint32_t kind, void *hip_stream, const df11_launch *launch);

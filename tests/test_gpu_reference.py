@@ -1,7 +1,8 @@
 """GPU checks of the bandwidth references (df11_bandwidth_reference): the
 two streaming kernels that move a decode's HBM bytes without decoding write
-out[i] = weight i with its exponent field zero, for every i, and nothing
-outside the output, for any size, output offset and launch geometry."""
+out[i] = weight i with its exponent field zero, for every i, the writes-only
+one zeros, the reads-only one nothing, and none writes outside the output,
+for any size, output offset and launch geometry."""
 import numpy as np
 import pytest
 
@@ -11,7 +12,18 @@ import huffman_decode_block_amd as hdb
 pytestmark = pytest.mark.gpu
 
 GUARD = 64
-KINDS = {"skeleton": hdb.DF11_REFERENCE_SKELETON, "stream": hdb.DF11_REFERENCE_STREAM}
+KINDS = {"skeleton": hdb.DF11_REFERENCE_SKELETON, "stream": hdb.DF11_REFERENCE_STREAM,
+         "writes": hdb.DF11_REFERENCE_WRITES, "reads": hdb.DF11_REFERENCE_READS}
+FILL = 0x5A5A
+
+
+def expected(kname, x):
+    """What a reference leaves in an output pre-filled with FILL."""
+    if kname == "writes":
+        return np.zeros_like(x)
+    if kname == "reads":
+        return np.full_like(x, FILL)
+    return x & np.uint16(0x807F)
 
 
 def say(msg):
@@ -26,12 +38,12 @@ def torch():
 
 
 def run_guarded(torch, blk, n, kind, lead=GUARD, launch=None):
-    buf = torch.full((n + lead + GUARD,), 0x5A5A, dtype=torch.int16, device="cuda")
+    buf = torch.full((n + lead + GUARD,), FILL, dtype=torch.int16, device="cuda")
     hdb.df11_bandwidth_reference(blk, buf[lead:lead + n], kind, launch=launch)
     torch.cuda.synchronize()
     h = buf.cpu().numpy().view(np.uint16)
-    assert (h[:lead] == 0x5A5A).all(), "write below the output"
-    assert (h[lead + n:] == 0x5A5A).all(), "write past the output"
+    assert (h[:lead] == FILL).all(), "write below the output"
+    assert (h[lead + n:] == FILL).all(), "write past the output"
     return h[lead:lead + n]
 
 
@@ -40,7 +52,7 @@ def check(torch, x, name, lead=GUARD, launch=None):
     for kname, kind in KINDS.items():
         say(f"{name}: {kname} n={x.size} lead={lead} launch={launch}")
         y = run_guarded(torch, blk, x.size, kind, lead, launch)
-        np.testing.assert_array_equal(y, x & np.uint16(0x807F))
+        np.testing.assert_array_equal(y, expected(kname, x))
 
 
 @pytest.mark.parametrize("n", [1, 7, 8, 4095, 4096, 4097, 65_535, 1_000_003])
@@ -74,10 +86,11 @@ def test_reference_full_c3(torch):
     out = torch.empty(x.size, dtype=torch.int16, device="cuda")
     for kname, kind in KINDS.items():
         say(f"C3: {kname}")
-        out.fill_(0x5A5A)
+        out.fill_(FILL)
         hdb.df11_bandwidth_reference(blk, out, kind)
         torch.cuda.synchronize()
-        assert torch.equal(out, expect)
+        want = {"writes": torch.zeros_like(out), "reads": torch.full_like(out, FILL)}.get(kname, expect)
+        assert torch.equal(out, want)
 
 
 def test_reference_refuses_format_variants_and_unknown_kinds(torch):
