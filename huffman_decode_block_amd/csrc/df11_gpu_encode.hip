@@ -603,8 +603,10 @@ __global__ void __launch_bounds__(kRunThreads) __attribute__((amdgpu_waves_per_e
         uint32_t ex[16];
 #pragma unroll
         for (uint32_t j = 0; j < 16; ++j) ex[j] = stage[17 * lane + j];
-        const uint64_t l0 = c * kChunk + uint64_t{kRunPer} * lane;  // the lane's first weight
-        const uint32_t m = full ? kRunPer : (l0 < p.n ? static_cast<uint32_t>(p.n - l0 < kRunPer ? p.n - l0 : kRunPer) : 0u);
+        const uint64_t first0 = c * kChunk + uint64_t{kRunPer} * lane;  // the lane's first weight
+        const uint32_t m = full ? kRunPer
+                                : (first0 < p.n ? static_cast<uint32_t>(p.n - first0 < kRunPer ? p.n - first0 : kRunPer)
+                                                : 0u);
         uint32_t sum = 0, lastlen = 0;
         if (full) {  // uniform
 #pragma unroll
@@ -634,7 +636,6 @@ __global__ void __launch_bounds__(kRunThreads) __attribute__((amdgpu_waves_per_e
         // the first window boundary at or after the previous code's start: a
         // code starting there or later opens a window
         int32_t nwb = ((static_cast<int32_t>(pos0) - static_cast<int32_t>(prevlen)) >> 6) * 64 + 64;
-        const uint64_t first0 = c * kChunk + uint64_t{kRunPer} * lane;
         const uint32_t k0 = head >> 5;
         const uint32_t nwords = (head + chunk_bits + 31) >> 5;
         const bool head_shared = (cb & 31u) != 0;
