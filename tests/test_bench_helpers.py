@@ -118,3 +118,15 @@ def test_cold_schedule_rejects_an_unknown_flush(bench):
     with pytest.raises(ValueError):
         bench.ColdSchedule("cpu", None, "write-1gib")
     assert bench.ColdSchedule.FLUSH_KINDS[0] == "read"  # the headline schedule is the default
+
+
+def test_committed_counters_describe_the_current_decode_kernel(bench):
+    """The headline's roofline.traffic comes from the committed counter
+    summary only while it was taken on the current decode kernel code (its
+    source and the headers it includes): a change to any of them needs the
+    counters taken again."""
+    with open(bench.COUNTERS) as f:
+        c = json.load(f)
+    assert c["kernel_code_sha256_16"] == bench.kernel_hash(), \
+        "the decode kernel's code changed since profiles/df11_decode_kernel_c3_hbm_counters.json was taken"
+    assert bench.measured_traffic("C3") == c["hbm_bytes_per_launch"]
