@@ -184,6 +184,28 @@ def test_histogram_window_follows_each_waves_chunks(torch):
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("counts", [False, True])
+def test_pack_paths_meet_at_chunk_boundaries(torch, counts):
+    """Chunks of rare exponents (long codes, more bits than a wave's LDS frame
+    holds) between chunks of common ones: the pack pass ORs the former's codes
+    into HBM one by one and packs the latter in LDS, and the words and windows
+    they share at their boundaries must come out as the host encoder's."""
+    chunk = 4096
+    x = di.random_normal(40 * chunk + 1000, 0.02, 41)
+    rng = np.random.default_rng(42)
+    rare = np.concatenate([np.arange(1, 100), np.arange(140, 255)]).astype(np.uint16)
+    slow = (3, 4, 17, 38)
+    for c in slow:
+        e = rng.choice(rare, chunk)
+        sm = rng.integers(0, 1 << 16, chunk, dtype=np.uint16) & np.uint16(0x807F)
+        x[c * chunk:(c + 1) * chunk] = sm | (e << np.uint16(7))
+    g = check(torch, x, f"paths_meet_counts{int(counts)}", counts=counts)
+    lens = np.frombuffer(bytes(g.plan.code_len), dtype=np.uint8).astype(np.int64)
+    bits = [int(lens[(x[c * chunk:(c + 1) * chunk] >> 7) & 0xFF].sum()) for c in range(40)]
+    assert all(bits[c] > 32 * 1023 for c in slow), bits  # past the frame: the global path
+    assert all(bits[c] < 32 * 1000 for c in range(40) if c not in slow), bits  # the LDS frame
+
+
 def test_workload_c2(torch):
     check(torch, di.generate("C2"), "C2", counts=True)
 
