@@ -406,9 +406,9 @@ __global__ void __launch_bounds__(kThreads) bounds_kernel(EncParams p) {
 
 // ---------------------------------------------------------------- pack
 // Persistent waves, each packing one 4,096-weight chunk at a time with no
-// workgroup barrier: lane l takes weights
-// 64 l .. 64 l + 63 of the chunk, whose codes form one run of at least 64
-// bits, so that a 32-bit word is shared by two neighbouring lanes at most.
+// workgroup barrier: lane l takes weights 64 l .. 64 l + 63 of the chunk,
+// whose codes form one run of at least 64 bits, so that a 32-bit word is
+// shared by two neighbouring lanes at most.
 // The lane shifts its codes one after the other into a 64-bit register and
 // writes the last finished word into the wave's LDS frame after each code;
 // its first word, which the lane before also reaches into, is completed by
